@@ -1,0 +1,252 @@
+// api.hip -- host side of the C ABI declared in include/moe.h: argument
+// validation, workspace layout, and the order of kernel launches.
+#include <string.h>
+
+#include <vector>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int hip_fail(hipError_t e) {
+    g_last_hip = e;
+    return MOE_ERR_HIP;
+}
+
+// ---- stage timing -----------------------------------------------------------
+struct Profiler {
+    bool on = false;
+    int cap = 0, used = 0;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> stage;
+} g_prof;
+
+struct StageScope {
+    hipStream_t s;
+    int idx = -1;
+    StageScope(int stage, hipStream_t st) : s(st) {
+        if (!g_prof.on || g_prof.used >= g_prof.cap) return;
+        idx = g_prof.used++;
+        g_prof.stage[idx] = stage;
+        hipEventRecord(g_prof.ev[2 * idx], s);
+    }
+    ~StageScope() {
+        if (idx >= 0) hipEventRecord(g_prof.ev[2 * idx + 1], s);
+    }
+};
+
+// ---- validation ----------------------------------------------------------------
+int validate(const moe_config *c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->T < 1 || c->d_model < 1 || c->n_routed < 1 || c->n_routed > 1024) return MOE_ERR_INVALID_ARG;
+    if (c->top_k < 1 || c->top_k > c->n_routed || c->top_k > 16) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared < 0 || c->n_shared > 64 || c->d_ff < 1) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared > 0 && c->d_ff_shared < 1) return MOE_ERR_INVALID_ARG;
+    if (c->scoring < MOE_SCORE_SOFTMAX || c->scoring > MOE_ROUTE_HASH) return MOE_ERR_INVALID_ARG;
+    if (c->renorm != 0 && c->renorm != 1) return MOE_ERR_INVALID_ARG;
+    if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (c->flags & ~(MOE_LOGITS_IN | MOE_LOGITS_OUT)) return MOE_ERR_INVALID_ARG;
+    if ((c->flags & MOE_LOGITS_IN) && (c->flags & MOE_LOGITS_OUT)) return MOE_ERR_INVALID_ARG;
+    if (c->scoring == MOE_ROUTE_HASH && (c->top_k != 1 || c->flags)) return MOE_ERR_INVALID_ARG;
+    if (c->d_model % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
+    if (c->n_shared > 0 && c->d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
+    const long long P = (long long)c->T * c->top_k;
+    if (P > (1ll << 22)) return MOE_ERR_UNSUPPORTED;
+    if ((long long)c->T * c->d_model > (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t route_ws(const moe_config &c) {
+    if (c.scoring == MOE_ROUTE_HASH) return 0;
+    return ((size_t)c.T * c.n_routed * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t pstat_bytes(const moe_config &c) {
+    if (c.scoring == MOE_ROUTE_HASH) return 0;
+    return (size_t)select_blocks(c) * c.n_routed * sizeof(double);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config *cfg, int which) {
+    if (validate(cfg) != MOE_OK) return 0;
+    switch (which) {
+        case MOE_WS_ROUTE: return route_ws(*cfg);
+        case MOE_WS_FORWARD: return fwd_layout(*cfg).total;
+        case MOE_WS_PSTAT: return pstat_bytes(*cfg);
+        default: return 0;
+    }
+}
+
+int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const float *logit_offset,
+              const float *bias, const uint32_t *token_ids, float *logits, int32_t *topk_idx,
+              float *topk_w, int32_t *expert_counts, void *p_partial, void *workspace,
+              size_t ws_bytes, void *stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    const moe_config &c = *cfg;
+    if (!topk_idx || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (c.scoring == MOE_ROUTE_HASH) {
+        if (!token_ids || p_partial || logits) return MOE_ERR_INVALID_ARG;
+        StageScope sc(MOE_STAGE_SELECT, s);
+        if ((e = launch_fill_i32(expert_counts, c.n_routed, 0, s)) != hipSuccess) return hip_fail(e);
+        if ((e = launch_hash_route(c, token_ids, topk_idx, topk_w, expert_counts, s)) != hipSuccess)
+            return hip_fail(e);
+        return MOE_OK;
+    }
+    float *lg = logits;
+    if (c.flags & MOE_LOGITS_IN) {
+        if (!logits) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (!x || !w_gate) return MOE_ERR_INVALID_ARG;
+        if (c.flags & MOE_LOGITS_OUT) {
+            if (!logits) return MOE_ERR_INVALID_ARG;
+        } else {
+            if (logits) return MOE_ERR_INVALID_ARG;
+            if (!workspace) return MOE_ERR_INVALID_ARG;
+            if (ws_bytes < route_ws(c)) return MOE_ERR_WORKSPACE;
+            lg = (float *)workspace;
+        }
+        StageScope sc(MOE_STAGE_ROUTER_GEMM, s);
+        if ((e = launch_router_logits(c, x, w_gate, lg, s)) != hipSuccess) return hip_fail(e);
+    }
+    StageScope sc(MOE_STAGE_SELECT, s);
+    if ((e = launch_fill_i32(expert_counts, c.n_routed, 0, s)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_select(c, lg, logit_offset, bias, topk_idx, topk_w, expert_counts,
+                           (double *)p_partial, s)) != hipSuccess)
+        return hip_fail(e);
+    return MOE_OK;
+}
+
+int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, const float *topk_w,
+                const void *w13, const void *w2, const void *w13_shared, const void *w2_shared,
+                void *h, void *workspace, size_t ws_bytes, void *stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    const moe_config &c = *cfg;
+    if (!x || !topk_idx || !topk_w || !w13 || !w2 || !h || !workspace) return MOE_ERR_INVALID_ARG;
+    if (c.n_shared > 0 && (!w13_shared || !w2_shared)) return MOE_ERR_INVALID_ARG;
+    if (h == x) return MOE_ERR_INVALID_ARG;
+    const FwdLayout L = fwd_layout(c);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    hipError_t e;
+    {
+        StageScope sc(MOE_STAGE_PERMUTE, s);
+        if ((e = launch_permute(c, L, topk_idx, ws, s)) != hipSuccess) return hip_fail(e);
+    }
+    const MetaIdx mi = meta_index(L.G);
+    const int32_t *meta = (const int32_t *)(ws + L.off_meta);
+    GroupedArgs a;
+    a.T = c.T;
+    a.d = c.d_model;
+    a.top_k = c.top_k;
+    a.n_routed = c.n_routed;
+    a.n_shared = c.n_shared;
+    a.f = c.d_ff;
+    a.fs = c.n_shared > 0 ? c.d_ff_shared : 64;
+    a.G = L.G;
+    a.split_r = z_split_routed(c) ? 1 : 0;
+    a.split_s = z_split_shared(c) ? 1 : 0;
+    a.group_off = meta + mi.group_off;
+    a.group_cnt = meta + mi.group_cnt;
+    a.perm = (const int32_t *)(ws + L.off_perm);
+    a.topk_w = topk_w;
+    a.x = x;
+    a.w13 = w13;
+    a.w2 = w2;
+    a.w13s = w13_shared;
+    a.w2s = w2_shared;
+    a.zr = ws + L.off_zr;
+    a.zs = ws + L.off_zs;
+    a.yr = (float *)(ws + L.off_yr);
+    a.ys = (float *)(ws + L.off_ys);
+    {
+        StageScope sc(MOE_STAGE_GATE_UP, s);
+        a.tile_base = meta + mi.tile1;
+        if ((e = launch_gate_up(c, a, s)) != hipSuccess) return hip_fail(e);
+    }
+    {
+        StageScope sc(MOE_STAGE_DOWN, s);
+        a.tile_base = meta + mi.tile2;
+        if ((e = launch_down(c, a, s)) != hipSuccess) return hip_fail(e);
+    }
+    {
+        StageScope sc(MOE_STAGE_COMBINE, s);
+        if ((e = launch_combine(c, x, topk_idx, a.yr, a.ys, h, s)) != hipSuccess) return hip_fail(e);
+    }
+    return MOE_OK;
+}
+
+int moe_balance_stats(const moe_config *cfg, const int32_t *expert_counts, const void *p_partial,
+                      float alpha1, float *f, float *P, float *loss, void *stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    const moe_config &c = *cfg;
+    if (!expert_counts || !f) return MOE_ERR_INVALID_ARG;
+    if ((P || loss) && (!p_partial || c.scoring == MOE_ROUTE_HASH)) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    StageScope sc(MOE_STAGE_STATS, s);
+    hipError_t e = launch_balance_stats(c, expert_counts, (P || loss) ? (const double *)p_partial : nullptr,
+                                        select_blocks(c), alpha1, f, P, loss, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration (sizes must be multiples of 64)";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return hipGetErrorString(g_last_hip);
+        default: return "unknown status";
+    }
+}
+
+int moe_profile_enable(int max_records) {
+    if (max_records < 1) return MOE_ERR_INVALID_ARG;
+    if ((int)g_prof.ev.size() < 2 * max_records) {
+        const size_t old = g_prof.ev.size();
+        g_prof.ev.resize(2 * (size_t)max_records);
+        for (size_t i = old; i < g_prof.ev.size(); ++i) {
+            hipError_t e = hipEventCreate(&g_prof.ev[i]);
+            if (e != hipSuccess) {
+                g_prof.ev.resize(i);
+                return hip_fail(e);
+            }
+        }
+    }
+    g_prof.stage.assign(max_records, 0);
+    g_prof.cap = max_records;
+    g_prof.used = 0;
+    g_prof.on = true;
+    return MOE_OK;
+}
+
+int moe_profile_collect(moe_stage_times *out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    memset(out, 0, sizeof *out);
+    g_prof.on = false;
+    for (int i = 0; i < g_prof.used; ++i) {
+        hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(e);
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(e);
+        out->launches[g_prof.stage[i]] += 1;
+        out->ms[g_prof.stage[i]] += ms;
+    }
+    g_prof.used = 0;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// combine.hip -- the sum of the DeepSeekMoE layer ("core design 2" equation
+// of the DeepSeekMoE notes):
+//   h_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx[t][k]}(u_t)
+// The gate-scaled routed outputs arrive in pair order (t K' + k), the summed
+// shared output per token.  Each thread adds four columns in a fixed order
+// (residual, shared, then k = 0..K'-1) in fp32 and rounds once, so the
+// result is the same bit pattern on every run (no atomics).
+#include "common.h"
+
+namespace moe {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int has_shared,
+                                                 const void *__restrict__ x,
+                                                 const int32_t *__restrict__ idx,
+                                                 const float *__restrict__ yr,
+                                                 const float *__restrict__ ys, void *__restrict__ h) {
+    const int ncb = (d / 4 + blockDim.x - 1) / blockDim.x;
+    const int t = blockIdx.x / ncb;
+    const int c = ((blockIdx.x % ncb) * blockDim.x + threadIdx.x) * 4;
+    if (c >= d) return;
+    const size_t o = (size_t)t * d + c;
+    float4 acc;
+    if (BF16) {
+        const uint2 v = *(const uint2 *)((const uint16_t *)x + o);
+        acc.x = bf16_to_f32((uint16_t)(v.x & 0xffffu));
+        acc.y = bf16_to_f32((uint16_t)(v.x >> 16));
+        acc.z = bf16_to_f32((uint16_t)(v.y & 0xffffu));
+        acc.w = bf16_to_f32((uint16_t)(v.y >> 16));
+    } else {
+        acc = *(const float4 *)((const float *)x + o);
+    }
+    if (has_shared) {
+        const float4 s = *(const float4 *)(ys + o);
+        acc.x += s.x;
+        acc.y += s.y;
+        acc.z += s.z;
+        acc.w += s.w;
+    }
+    for (int k = 0; k < K; ++k) {
+        const int e = idx[(size_t)t * K + k];
+        if (e < 0 || e >= N) continue;
+        const float4 y = *(const float4 *)(yr + ((size_t)t * K + k) * d + c);
+        acc.x += y.x;
+        acc.y += y.y;
+        acc.z += y.z;
+        acc.w += y.w;
+    }
+    if (BF16) {
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+        v.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+        *(uint2 *)((uint16_t *)h + o) = v;
+    } else {
+        *(float4 *)((float *)h + o) = acc;
+    }
+}
+
+hipError_t launch_combine(const moe_config &c, const void *x, const int32_t *idx, const float *yr,
+                          const float *ys, void *h, hipStream_t s) {
+    dim3 grid(((c.d_model / 4 + 255) / 256) * c.T);
+    if (c.dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, c.T, c.d_model, c.top_k,
+                           c.n_routed, c.n_shared > 0, x, idx, yr, ys, h);
+    else
+        hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, c.T, c.d_model, c.top_k,
+                           c.n_routed, c.n_shared > 0, x, idx, yr, ys, h);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,127 @@
+// common.h -- device helpers and the launch interface shared by the HIP
+// sources of libmoe.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- element types --------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kXcds = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---- wave reductions (64 lanes) --------------------------------------------
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// ---- forward workspace layout ----------------------------------------------
+// Groups: g < N' are the routed experts (rows = the (token, slot) pairs that
+// chose g, in pair order); g == N' (present when K_s > 0) is every shared
+// expert at once (rows = all tokens, hidden width K_s * d_ff_shared).
+struct FwdLayout {
+    int n_chunks;       // permutation chunks
+    int chunk;          // pairs per chunk
+    int G;              // groups
+    size_t off_chunk;   // int32 [n_chunks][N']: per-chunk counts, then bases
+    size_t off_meta;    // int32 meta block (see MetaIdx)
+    size_t off_perm;    // int32 [T*K']: pair id at each expert-ordered row
+    size_t off_zr;      // [T*K'][d_ff] dtype: routed hidden activations
+    size_t off_zs;      // [T][K_s*d_ff_shared] dtype: shared hidden activations
+    size_t off_yr;      // fp32 [T*K'][d]: gate-scaled routed outputs, pair order
+    size_t off_ys;      // fp32 [T][d]: summed shared-expert outputs
+    size_t total;
+};
+
+// Offsets (in int32 elements) of the arrays inside the meta block.
+struct MetaIdx {
+    int group_off, group_cnt, tile1, tile2, bad, size;
+};
+__host__ __device__ inline MetaIdx meta_index(int G) {
+    MetaIdx m;
+    m.group_off = 0;
+    m.group_cnt = G + 1;
+    m.tile1 = 2 * G + 2;
+    m.tile2 = 3 * G + 3;
+    m.bad = 4 * G + 4;
+    m.size = 4 * G + 8;
+    return m;
+}
+
+// Tile shapes the permutation kernel prepares work lists for.
+struct TileShape {
+    int bm1, bz1;  // gate/up GEMM: rows per tile, hidden columns per tile
+    int bm2, bn2;  // down GEMM: rows per tile, output columns per tile
+};
+
+// Arguments of the grouped expert GEMMs.
+struct GroupedArgs {
+    int T, d, top_k, n_routed, n_shared, f, fs, G;
+    int split_r, split_s;     // hidden activation carried as a bf16 (hi, lo) pair
+    const int32_t *group_off, *group_cnt, *tile_base;
+    const int32_t *perm;      // pair id per expert-ordered row
+    const float *topk_w;      // [T*K']
+    const void *x, *w13, *w2, *w13s, *w2s;
+    void *zr, *zs;
+    float *yr, *ys;
+};
+
+// ---- launchers (each returns hipSuccess or the launch error) ---------------
+hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
+                                float *logits, hipStream_t s);
+hipError_t launch_select(const moe_config &c, const float *logits, const float *offset,
+                         const float *bias, int32_t *idx, float *w, int32_t *counts,
+                         double *p_partial, hipStream_t s);
+hipError_t launch_hash_route(const moe_config &c, const uint32_t *tid, int32_t *idx,
+                             float *w, int32_t *counts, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
+hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts,
+                                const double *p_partial, int n_blocks, float alpha1,
+                                float *f, float *P, float *loss, hipStream_t s);
+int select_blocks(const moe_config &c);   // blocks of the select kernel
+
+// Whether a group's hidden activation z is stored as two bf16 planes
+// (hi = bf16(z), lo = bf16(z - hi)) so that the down projection sees z to
+// about 16 significant bits: done where the gate is 1 (the shared experts,
+// and routed experts when K' = 1), since there a bf16 rounding of z would
+// reach h unscaled.
+inline bool z_split_shared(const moe_config &c) { return c.dtype == MOE_BF16 && c.n_shared > 0; }
+inline bool z_split_routed(const moe_config &c) { return c.dtype == MOE_BF16 && c.top_k == 1; }
+
+FwdLayout fwd_layout(const moe_config &c);
+TileShape tile_shape(const moe_config &c);
+hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t *idx,
+                          char *ws, hipStream_t s);
+hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a, hipStream_t s);
+hipError_t launch_down(const moe_config &c, const GroupedArgs &a, hipStream_t s);
+hipError_t launch_combine(const moe_config &c, const void *x, const int32_t *idx,
+                          const float *yr, const float *ys, void *h, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

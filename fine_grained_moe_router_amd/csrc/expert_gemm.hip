@@ -1,0 +1,362 @@
+// expert_gemm.hip -- the grouped expert contractions of the DeepSeekMoE layer.
+//
+// Every routed expert and the shared experts are SwiGLU FFNs,
+// W2 (SiLU(W1 u) * (W3 u)) (the 3-matrix form named in the MoE tutorial at
+// ai.clawlihai.cn); the layer is the "core design 2" equation of the
+// DeepSeekMoE notes.  Two launches:
+//   gate/up:  z = SiLU(X_e W1_e^T) * (X_e W3_e^T)   for each group e
+//   down:     y = z W2_e^T (routed rows scaled by their gate)
+// Group e < N' owns the pairs routed to expert e (rows gathered from x on
+// load, in the expert-contiguous order built by permute.hip).  Group N'
+// holds all K_s shared experts at once: every token is a row, and the K_s
+// hidden blocks of width d_ff_shared sit side by side (K_s shared experts
+// of width f act as one of width K_s f), so the down projection sums them
+// inside one K loop.
+//
+// Scheduling: persistent blocks.  Logical tiles are ordered (group, column
+// tile, row tile) with the row tile fastest, so the row tiles that share a
+// weight tile are adjacent.  The logical range is cut into 8 contiguous
+// pieces, one per XCD (block b runs on XCD b % 8), so adjacent tiles share
+// that XCD's L2.  Every block walks a bounded range and exits.
+#include "common.h"
+#include "mfma_tile.h"
+#include "simt_tile.h"
+
+namespace moe {
+
+enum { kGateUp = 0, kDown = 1 };
+
+__device__ __forceinline__ int find_group(const int32_t *__restrict__ base, int G, int tile) {
+    int lo = 0, hi = G;  // base[lo] <= tile < base[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (base[mid] <= tile) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+struct TileJob {
+    int g, i, j, row0, nrows;
+    bool shared;
+};
+
+__device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, int bm) {
+    TileJob t;
+    t.g = find_group(a.tile_base, a.G, tile);
+    const int rel = tile - a.tile_base[t.g];
+    const int cnt = a.group_cnt[t.g];
+    const int mt = (cnt + bm - 1) / bm;
+    t.j = rel / mt;
+    t.i = rel - t.j * mt;
+    t.row0 = t.i * bm;
+    t.nrows = min(bm, cnt - t.row0);
+    t.shared = (t.g == a.n_routed);
+    return t;
+}
+
+// Block b's share of the logical tiles: XCD b % 8 takes one contiguous
+// eighth; its blocks stride through it.
+struct TileRange {
+    int first, end, step;
+};
+__device__ __forceinline__ TileRange tile_range(int total) {
+    const int xcd = blockIdx.x % kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int nslots = gridDim.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int start = xcd * per;
+    TileRange r;
+    r.first = start + slot;
+    r.end = min(total, start + per);
+    r.step = nslots;
+    return r;
+}
+
+// ---------------------------------------------------------------- bf16 MFMA
+
+constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;
+using GateUpTile = MfmaTile<kBM, kBN, kWM, kWN, true>;
+using DownTile = MfmaTile<kBM, kBN, kWM, kWN, false>;
+
+__global__ __launch_bounds__(GateUpTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
+    using Tl = GateUpTile;
+    __shared__ u32x4 As[2 * Tl::LDS_A];
+    __shared__ u32x4 Bs[2 * Tl::LDS_B];
+    const TileRange tr = tile_range(a.tile_base[a.G]);
+    const uint16_t *x = (const uint16_t *)a.x;
+    const int fsum = a.n_shared * a.fs;
+    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
+        const TileJob tj = decode_tile(a, tile, kBM);
+        const int zc0 = tj.j * (kBN / 2);   // first hidden column of the tile
+        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        const uint16_t *arow[Tl::A_LD];
+        const uint16_t *brow[Tl::B_LD];
+#pragma unroll
+        for (int l = 0; l < Tl::A_LD; ++l) {
+            const int r = Tl::load_row(threadIdx.x, l);
+            const uint16_t *p = nullptr;
+            if (r < tj.nrows) {
+                const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
+                p = x + (size_t)tok * a.d;
+            }
+            arow[l] = p;
+        }
+        const uint16_t *wbase;
+        int wrow0, wup;
+        if (tj.shared) {
+            const int js = zc0 / a.fs;
+            wbase = (const uint16_t *)a.w13s + (size_t)js * 2 * a.fs * a.d;
+            wrow0 = zc0 - js * a.fs;
+            wup = a.fs;
+        } else {
+            wbase = (const uint16_t *)a.w13 + (size_t)tj.g * 2 * a.f * a.d;
+            wrow0 = zc0;
+            wup = a.f;
+        }
+#pragma unroll
+        for (int l = 0; l < Tl::B_LD; ++l) {
+            const int r = Tl::load_row(threadIdx.x, l);
+            const int wr = (r < kBN / 2) ? wrow0 + r : wup + wrow0 + (r - kBN / 2);
+            brow[l] = wbase + (size_t)wr * a.d;
+        }
+        f32x16 acc[Tl::FM][Tl::FN];
+        Tl::run(arow, brow, a.d, 0, 1, 0, As, Bs, acc);
+        // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for
+        // a split group the residual z - hi goes, rounded, zw columns further.
+        uint16_t *zout = (uint16_t *)(tj.shared ? a.zs : a.zr);
+        const int zw = tj.shared ? fsum : a.f;
+        const int split = tj.shared ? a.split_s : a.split_r;
+        const size_t zstride = (size_t)zw * (split ? 2 : 1);
+        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+#pragma unroll
+        for (int i = 0; i < Tl::FM; ++i)
+#pragma unroll
+            for (int h = 0; h < Tl::FN / 2; ++h) {
+                const int col = zc0 + Tl::out_col(h);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = Tl::out_row(i, r);
+                    if (row < tj.nrows) {
+                        const float ga = acc[i][h][r];
+                        const float up = acc[i][h + Tl::FN / 2][r];
+                        const float z = ga / (1.0f + __expf(-ga)) * up;
+                        const uint16_t hi = f32_to_bf16(z);
+                        uint16_t *dst = zout + (rbase + row) * zstride + col;
+                        dst[0] = hi;
+                        if (split) dst[zw] = f32_to_bf16(z - bf16_to_f32(hi));
+                    }
+                }
+            }
+    }
+}
+
+__global__ __launch_bounds__(DownTile::NT) void k_down_bf16(const GroupedArgs a) {
+    using Tl = DownTile;
+    __shared__ u32x4 As[2 * Tl::LDS_A];
+    __shared__ u32x4 Bs[2 * Tl::LDS_B];
+    const TileRange tr = tile_range(a.tile_base[a.G]);
+    const int fsum = a.n_shared * a.fs;
+    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
+        const TileJob tj = decode_tile(a, tile, kBM);
+        const int n0 = tj.j * kBN;
+        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        // K runs over z, or over (hi, lo) of a split group, reusing W2
+        const int split = tj.shared ? a.split_s : a.split_r;
+        const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
+        const uint16_t *zin = (const uint16_t *)(tj.shared ? a.zs : a.zr);
+        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+        const uint16_t *arow[Tl::A_LD];
+        const uint16_t *brow[Tl::B_LD];
+#pragma unroll
+        for (int l = 0; l < Tl::A_LD; ++l) {
+            const int r = Tl::load_row(threadIdx.x, l);
+            arow[l] = (r < tj.nrows) ? zin + (rbase + r) * K : nullptr;
+        }
+#pragma unroll
+        for (int l = 0; l < Tl::B_LD; ++l) {
+            const int n = n0 + Tl::load_row(threadIdx.x, l);
+            const uint16_t *p = nullptr;
+            if (n < a.d)
+                p = tj.shared ? (const uint16_t *)a.w2s + (size_t)n * a.fs
+                              : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f + (size_t)n * a.f;
+            brow[l] = p;
+        }
+        f32x16 acc[Tl::FM][Tl::FN];
+        if (tj.shared)
+            Tl::run(arow, brow, K, a.fs, a.n_shared, (size_t)a.d * a.fs, As, Bs, acc);
+        else
+            Tl::run(arow, brow, K, split ? a.f : 0, 1, 0, As, Bs, acc);
+#pragma unroll
+        for (int i = 0; i < Tl::FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = Tl::out_row(i, r);
+                if (row >= tj.nrows) continue;
+                float *dst;
+                float gate = 1.0f;
+                if (tj.shared) {
+                    dst = a.ys + (size_t)(tj.row0 + row) * a.d;
+                } else {
+                    const int pair = a.perm[rbase + row];
+                    gate = a.topk_w[pair];
+                    dst = a.yr + (size_t)pair * a.d;
+                }
+#pragma unroll
+                for (int j = 0; j < Tl::FN; ++j) {
+                    const int col = n0 + Tl::out_col(j);
+                    if (col < a.d) dst[col] = gate * acc[i][j][r];
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------- fp32 SIMT
+
+__global__ __launch_bounds__(256) void k_gate_up_f32(const GroupedArgs a) {
+    __shared__ float As[kSBK * kSPad], Bs[kSBK * kSPad];
+    const TileRange tr = tile_range(a.tile_base[a.G]);
+    const float *x = (const float *)a.x;
+    const int fsum = a.n_shared * a.fs;
+    const int lr = threadIdx.x >> 2;
+    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
+        const TileJob tj = decode_tile(a, tile, 64);
+        const int zc0 = tj.j * 32;
+        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        const float *arow = nullptr;
+        if (lr < tj.nrows) {
+            const int tok = tj.shared ? tj.row0 + lr : a.perm[goff + tj.row0 + lr] / a.top_k;
+            arow = x + (size_t)tok * a.d;
+        }
+        const float *wbase;
+        int wrow0, wup;
+        if (tj.shared) {
+            const int js = zc0 / a.fs;
+            wbase = (const float *)a.w13s + (size_t)js * 2 * a.fs * a.d;
+            wrow0 = zc0 - js * a.fs;
+            wup = a.fs;
+        } else {
+            wbase = (const float *)a.w13 + (size_t)tj.g * 2 * a.f * a.d;
+            wrow0 = zc0;
+            wup = a.f;
+        }
+        const int wr = (lr < 32) ? wrow0 + lr : wup + wrow0 + (lr - 32);
+        const float *brow = wbase + (size_t)wr * a.d;
+        float acc[4][4];
+        SimtTile<true>::run(arow, brow, a.d, 0, 1, 0, As, Bs, acc);
+        float *zout = (float *)(tj.shared ? a.zs : a.zr);
+        const int zw = tj.shared ? fsum : a.f;
+        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = SimtTile<true>::out_row(i);
+            if (row >= tj.nrows) continue;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float ga = acc[i][j], up = acc[i][j + 2];
+                zout[(rbase + row) * zw + zc0 + SimtTile<true>::out_col(j)] =
+                    ga / (1.0f + expf(-ga)) * up;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_down_f32(const GroupedArgs a) {
+    __shared__ float As[kSBK * kSPad], Bs[kSBK * kSPad];
+    const TileRange tr = tile_range(a.tile_base[a.G]);
+    const int fsum = a.n_shared * a.fs;
+    const int lr = threadIdx.x >> 2;
+    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
+        const TileJob tj = decode_tile(a, tile, 64);
+        const int n0 = tj.j * 64;
+        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        const int K = tj.shared ? fsum : a.f;
+        const float *zin = (const float *)(tj.shared ? a.zs : a.zr);
+        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+        const float *arow = (lr < tj.nrows) ? zin + (rbase + lr) * K : nullptr;
+        const int n = n0 + lr;
+        const float *brow = nullptr;
+        if (n < a.d)
+            brow = tj.shared ? (const float *)a.w2s + (size_t)n * a.fs
+                             : (const float *)a.w2 + (size_t)tj.g * a.d * a.f + (size_t)n * a.f;
+        float acc[4][4];
+        SimtTile<false>::run(arow, brow, K, tj.shared ? a.fs : 0, a.n_shared, (size_t)a.d * a.fs,
+                             As, Bs, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = SimtTile<false>::out_row(i);
+            if (row >= tj.nrows) continue;
+            float *dst;
+            float gate = 1.0f;
+            if (tj.shared) {
+                dst = a.ys + (size_t)(tj.row0 + row) * a.d;
+            } else {
+                const int pair = a.perm[rbase + row];
+                gate = a.topk_w[pair];
+                dst = a.yr + (size_t)pair * a.d;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + SimtTile<false>::out_col(j);
+                if (col < a.d) dst[col] = gate * acc[i][j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Persistent grid: as many blocks as fit at once (per_cu per CU), no more than
+// the largest possible tile count, a multiple of the XCD count.
+static int persistent_grid(long long max_tiles, int per_cu) {
+    long long g = (long long)device_cu_count() * per_cu;
+    if (g > max_tiles) g = max_tiles;
+    g = (g + kXcds - 1) / kXcds * kXcds;
+    return (int)(g < kXcds ? kXcds : g);
+}
+
+static long long max_tiles(const moe_config &c, int bm, int ncols_tile, int width_r, int width_s) {
+    const long long P = (long long)c.T * c.top_k;
+    long long rt = (P + bm - 1) / bm + c.n_routed;  // sum over experts of ceil(cnt / bm)
+    long long n = rt * ((width_r + ncols_tile - 1) / ncols_tile);
+    if (c.n_shared > 0) n += ((c.T + bm - 1) / bm) * ((width_s + ncols_tile - 1) / ncols_tile);
+    return n;
+}
+
+hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a, hipStream_t s) {
+    const TileShape ts = tile_shape(c);
+    const long long mt = max_tiles(c, ts.bm1, ts.bz1, c.d_ff, c.n_shared * c.d_ff_shared);
+    if (c.dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_gate_up_bf16, dim3(persistent_grid(mt, 2)), dim3(GateUpTile::NT), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL(k_gate_up_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const moe_config &c, const GroupedArgs &a, hipStream_t s) {
+    const TileShape ts = tile_shape(c);
+    const long long mt = max_tiles(c, ts.bm2, ts.bn2, c.d_model, c.d_model);
+    if (c.dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_down_bf16, dim3(persistent_grid(mt, 2)), dim3(DownTile::NT), 0, s,
+                           a);
+    else
+        hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

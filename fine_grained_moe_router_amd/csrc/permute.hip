@@ -1,0 +1,186 @@
+// permute.hip -- expert histogram, prefix scan and stable permutation of the
+// (token, slot) pairs into expert-contiguous order, plus the work lists of
+// the two grouped expert GEMMs.  Everything stays on the device: no count
+// ever travels to the host.
+//
+// The gate matrix g of the DeepSeekMoE notes is sparse (K' non-zeros per
+// token, top-k gate equation); it arrives as topk_idx[T][K'].  Pair
+// p = t K' + k.  Expert e's rows are the pairs with topk_idx == e in
+// ascending p (a stable counting sort): chunk histograms, a scan over
+// (expert, chunk), then a per-chunk placement pass.
+#include "common.h"
+
+namespace moe {
+
+static int perm_chunk(int pairs) {
+    int per = (pairs + 255) / 256;   // at most 256 chunks
+    per = ((per + 255) / 256) * 256;
+    return per < 256 ? 256 : per;
+}
+
+TileShape tile_shape(const moe_config &c) {
+    if (c.dtype == MOE_BF16) return TileShape{128, 64, 128, 128};
+    return TileShape{64, 32, 64, 64};
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+FwdLayout fwd_layout(const moe_config &c) {
+    FwdLayout L;
+    const size_t P = (size_t)c.T * c.top_k;
+    const size_t eb = c.dtype == MOE_BF16 ? 2 : 4;
+    L.chunk = perm_chunk((int)P);
+    L.n_chunks = (int)((P + L.chunk - 1) / L.chunk);
+    L.G = c.n_routed + (c.n_shared > 0 ? 1 : 0);
+    size_t o = 0;
+    L.off_chunk = o;
+    o = align256(o + (size_t)L.n_chunks * c.n_routed * 4);
+    L.off_meta = o;
+    o = align256(o + (size_t)meta_index(L.G).size * 4);
+    L.off_perm = o;
+    o = align256(o + P * 4);
+    L.off_zr = o;
+    o = align256(o + P * c.d_ff * eb * (z_split_routed(c) ? 2 : 1));
+    L.off_zs = o;
+    o = align256(o + (size_t)c.T * c.n_shared * c.d_ff_shared * eb * (z_split_shared(c) ? 2 : 1));
+    L.off_yr = o;
+    o = align256(o + P * c.d_model * 4);
+    L.off_ys = o;
+    o = align256(o + (size_t)(c.n_shared > 0 ? c.T : 0) * c.d_model * 4);
+    L.total = o;
+    return L;
+}
+
+// Per-chunk histogram of routed expert ids.  Out-of-range ids are counted
+// in meta[bad] and otherwise ignored.
+__global__ __launch_bounds__(256) void k_perm_hist(int P, int N, int chunk,
+                                                   const int32_t *__restrict__ idx,
+                                                   int32_t *__restrict__ cc,
+                                                   int32_t *__restrict__ bad) {
+    extern __shared__ int32_t h[];
+    for (int e = threadIdx.x; e < N; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+    int nbad = 0;
+    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+        const int e = idx[p];
+        if (e >= 0 && e < N) atomicAdd(&h[e], 1);
+        else ++nbad;
+    }
+    if (nbad) atomicAdd(bad, nbad);
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) cc[(size_t)blockIdx.x * N + e] = h[e];
+}
+
+// Exclusive scan of data[0..n) (n <= 2 * blockDim.x) held in LDS; returns the
+// total.  tmp: blockDim.x ints of LDS.
+__device__ int block_excl_scan(int32_t *data, int n, int32_t *tmp) {
+    const int t = threadIdx.x;
+    const int a = (2 * t < n) ? data[2 * t] : 0;
+    const int b = (2 * t + 1 < n) ? data[2 * t + 1] : 0;
+    tmp[t] = a + b;
+    __syncthreads();
+    for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+        const int v = (t >= o) ? tmp[t - o] : 0;
+        __syncthreads();
+        tmp[t] += v;
+        __syncthreads();
+    }
+    const int excl = tmp[t] - (a + b);
+    const int total = tmp[blockDim.x - 1];
+    __syncthreads();
+    if (2 * t < n) data[2 * t] = excl;
+    if (2 * t + 1 < n) data[2 * t + 1] = excl + a;
+    __syncthreads();
+    return total;
+}
+
+// One block.  Turns chunk counts into chunk bases (relative to the expert),
+// computes group row counts/offsets and the tile prefix sums of both GEMMs.
+__global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, int n_shared,
+                                                    int f, int fsum, int d, TileShape ts,
+                                                    int32_t *__restrict__ cc,
+                                                    int32_t *__restrict__ meta) {
+    __shared__ int32_t cnt[2048], t1[2048], t2[2048], tmp[1024];
+    const int G = N + (n_shared > 0 ? 1 : 0);
+    const MetaIdx mi = meta_index(G);
+    for (int e = threadIdx.x; e < 2048; e += blockDim.x) {
+        cnt[e] = 0;
+        t1[e] = 0;
+        t2[e] = 0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        int run = 0;
+        for (int c = 0; c < n_chunks; ++c) {
+            const int v = cc[(size_t)c * N + e];
+            cc[(size_t)c * N + e] = run;
+            run += v;
+        }
+        cnt[e] = run;
+    }
+    if (threadIdx.x == 0 && n_shared > 0) cnt[N] = T;
+    __syncthreads();
+    const int ntn2 = (d + ts.bn2 - 1) / ts.bn2;
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+        const int c = cnt[g];
+        const int width = (g < N) ? f : fsum;
+        t1[g] = ((c + ts.bm1 - 1) / ts.bm1) * (width / ts.bz1);
+        t2[g] = ((c + ts.bm2 - 1) / ts.bm2) * ntn2;
+        meta[mi.group_cnt + g] = c;
+    }
+    __syncthreads();
+    const int tot1 = block_excl_scan(t1, G, tmp);
+    const int tot2 = block_excl_scan(t2, G, tmp);
+    // row offsets of the routed groups (the shared group reads rows 0..T-1)
+    if (threadIdx.x == 0 && n_shared > 0) cnt[N] = 0;
+    __syncthreads();
+    block_excl_scan(cnt, N, tmp);
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+        meta[mi.group_off + g] = (g < N) ? cnt[g] : 0;
+        meta[mi.tile1 + g] = t1[g];
+        meta[mi.tile2 + g] = t2[g];
+    }
+    if (threadIdx.x == 0) {
+        meta[mi.tile1 + G] = tot1;
+        meta[mi.tile2 + G] = tot2;
+    }
+}
+
+// Stable placement: thread e scans its chunk's ids in pair order and writes
+// every pair that chose e to the next row of expert e.
+__global__ __launch_bounds__(256) void k_perm_scatter(int P, int N, int chunk,
+                                                      const int32_t *__restrict__ idx,
+                                                      const int32_t *__restrict__ cc,
+                                                      const int32_t *__restrict__ group_off,
+                                                      int32_t *__restrict__ perm) {
+    extern __shared__ int32_t ids[];
+    const int p0 = blockIdx.x * chunk, n = min(P, p0 + chunk) - p0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) ids[i] = idx[p0 + i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        int pos = group_off[e] + cc[(size_t)blockIdx.x * N + e];
+        for (int i = 0; i < n; ++i)
+            if (ids[i] == e) perm[pos++] = p0 + i;
+    }
+}
+
+hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t *idx, char *ws,
+                          hipStream_t s) {
+    const int P = c.T * c.top_k;
+    const int N = c.n_routed;
+    int32_t *cc = (int32_t *)(ws + L.off_chunk);
+    int32_t *meta = (int32_t *)(ws + L.off_meta);
+    const MetaIdx mi = meta_index(L.G);
+    hipError_t e = launch_fill_i32(meta + mi.bad, 1, 0, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_perm_hist, dim3(L.n_chunks), dim3(256), (size_t)N * 4, s, P, N, L.chunk,
+                       idx, cc, meta + mi.bad);
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, L.n_chunks, c.T, c.n_shared,
+                       c.d_ff, c.n_shared * c.d_ff_shared, c.d_model, tile_shape(c), cc, meta);
+    hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
+                       L.chunk, idx, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm));
+    return hipGetLastError();
+}
+
+}  // namespace moe

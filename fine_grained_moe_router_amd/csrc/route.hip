@@ -1,0 +1,352 @@
+// route.hip -- the router of the DeepSeekMoE layer on gfx950:
+//   * router GEMM l = x W_g^T (gating network of the freedeepseekapi.com MoE
+//     blog, sec. 2): bf16 MFMA with fp32 accumulation, or fp32 SIMT;
+//   * per-token scoring, selection bias, top-K', gates, expert counts and
+//     per-block partial sums of the scores, one wavefront per token
+//     (top-k gate equation of the DeepSeekMoE reading notes; V4 book ch. 02
+//     sec. 1 sigmoid + renormalisation, sec. 2 sqrt(softplus), sec. 3 the
+//     selection-only bias);
+//   * hash routing (V4 book ch. 02 sec. 5);
+//   * the expert-level balance statistics f_i, P_i, L_ExpBal (DeepSeekMoE
+//     notes, "Expert-level balance loss").
+#include <math.h>
+
+#include "common.h"
+#include "mfma_tile.h"
+#include "simt_tile.h"
+
+namespace moe {
+
+// ============================================================ router GEMM
+
+using RouterTile = MfmaTile<64, 64, 2, 2, false>;
+
+__global__ __launch_bounds__(RouterTile::NT) void k_router_bf16(int T, int d, int N,
+                                                                const uint16_t *__restrict__ x,
+                                                                const uint16_t *__restrict__ wg,
+                                                                float *__restrict__ logits) {
+    __shared__ u32x4 As[2 * RouterTile::LDS_A];
+    __shared__ u32x4 Bs[2 * RouterTile::LDS_B];
+    const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+    const uint16_t *arow[RouterTile::A_LD];
+    const uint16_t *brow[RouterTile::B_LD];
+#pragma unroll
+    for (int i = 0; i < RouterTile::A_LD; ++i) {
+        int r = m0 + RouterTile::load_row(threadIdx.x, i);
+        arow[i] = (r < T) ? x + (size_t)r * d : nullptr;
+    }
+#pragma unroll
+    for (int i = 0; i < RouterTile::B_LD; ++i) {
+        int r = n0 + RouterTile::load_row(threadIdx.x, i);
+        brow[i] = (r < N) ? wg + (size_t)r * d : nullptr;
+    }
+    f32x16 acc[RouterTile::FM][RouterTile::FN];
+    RouterTile::run(arow, brow, d, 0, 1, 0, As, Bs, acc);
+#pragma unroll
+    for (int i = 0; i < RouterTile::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < RouterTile::FN; ++j) {
+            const int col = n0 + RouterTile::out_col(j);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + RouterTile::out_row(i, r);
+                if (row < T && col < N) logits[(size_t)row * N + col] = acc[i][j][r];
+            }
+        }
+}
+
+__global__ __launch_bounds__(256) void k_router_f32(int T, int d, int N, const float *__restrict__ x,
+                                                    const float *__restrict__ wg,
+                                                    float *__restrict__ logits) {
+    __shared__ float As[kSBK * kSPad], Bs[kSBK * kSPad];
+    const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+    const int lr = threadIdx.x >> 2;
+    const float *arow = (m0 + lr < T) ? x + (size_t)(m0 + lr) * d : nullptr;
+    const float *brow = (n0 + lr < N) ? wg + (size_t)(n0 + lr) * d : nullptr;
+    float acc[4][4];
+    SimtTile<false>::run(arow, brow, d, 0, 1, 0, As, Bs, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = m0 + SimtTile<false>::out_row(i), col = n0 + SimtTile<false>::out_col(j);
+            if (row < T && col < N) logits[(size_t)row * N + col] = acc[i][j];
+        }
+}
+
+hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
+                                float *logits, hipStream_t s) {
+    dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64);
+    if (c.dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_router_bf16, grid, dim3(RouterTile::NT), 0, s, c.T, c.d_model,
+                           c.n_routed, (const uint16_t *)x, (const uint16_t *)wg, logits);
+    else
+        hipLaunchKernelGGL(k_router_f32, grid, dim3(256), 0, s, c.T, c.d_model, c.n_routed,
+                           (const float *)x, (const float *)wg, logits);
+    return hipGetLastError();
+}
+
+// ============================================================ selection
+
+constexpr int kSelWaves = 4;
+constexpr int kMaxTopK = 16;
+
+int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 64 : 16; }
+
+int select_blocks(const moe_config &c) {
+    const int tpb = select_tokens_per_block(c);
+    return (c.T + tpb - 1) / tpb;
+}
+
+// Score of one expert, in double from the fp32 logit (V4 book ch. 02: sec. 1
+// sigmoid, sec. 2 sqrt(log(1 + e^l)) written so that it cannot overflow).
+__device__ __forceinline__ double score_pointwise(int scoring, float l) {
+    const double v = (double)l;
+    if (scoring == MOE_SCORE_SIGMOID) return 1.0 / (1.0 + exp(-v));
+    const double sp = v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));
+    return sqrt(sp);
+}
+
+// One wavefront per token.  Lane `lane` owns experts lane + 64 j, j < J.
+template <int J>
+__global__ __launch_bounds__(kSelWaves * kWave) void k_select(
+    int T, int N, int K, int scoring, int renorm, int tpb, const float *__restrict__ logits,
+    const float *__restrict__ offset, const float *__restrict__ bias, int32_t *__restrict__ idx_out,
+    float *__restrict__ w_out, int32_t *__restrict__ counts, double *__restrict__ p_partial) {
+    __shared__ int32_t hist[J * kWave];
+    __shared__ double psum[kSelWaves][J * kWave];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int e = threadIdx.x; e < J * kWave; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+
+    double pacc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) pacc[j] = 0.0;
+
+    const int t0 = blockIdx.x * tpb;
+    const int t1 = min(T, t0 + tpb);
+    for (int t = t0 + wave; t < t1; t += kSelWaves) {
+        float l[J], key[J], s32[J];
+        const float *row = logits + (size_t)t * N;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + 64 * j;
+            float v = (e < N) ? row[e] : -INFINITY;
+            if (offset && e < N) v = v + offset[e];  // fp32 add
+            l[j] = v;
+        }
+        // ---- scores: double from the fp32 logit, rounded once to fp32
+        if (scoring == MOE_SCORE_SOFTMAX) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < J; ++j) m = fmaxf(m, l[j]);
+            m = wave_max_f32(m);
+            double ex[J], part = 0.0;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int e = lane + 64 * j;
+                ex[j] = (e < N) ? exp((double)l[j] - (double)m) : 0.0;
+                part += ex[j];
+            }
+            const double sum = wave_sum_f64(part);
+#pragma unroll
+            for (int j = 0; j < J; ++j) s32[j] = (float)(ex[j] / sum);
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int e = lane + 64 * j;
+                s32[j] = (e < N) ? (float)score_pointwise(scoring, l[j]) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + 64 * j;
+            key[j] = bias ? ((e < N) ? s32[j] + bias[e] : -INFINITY) : l[j];  // fp32 add
+            if (e < N) pacc[j] += (double)s32[j];
+        }
+        // ---- top-K': K' rounds of a wave-wide argmax on (key desc, index asc)
+        uint32_t taken = 0;
+        int sel[kMaxTopK];
+        float sv[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            sel[k] = 0;
+            sv[k] = 0.0f;
+            if (k < K) {
+                float bk = -INFINITY;
+                int bi = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int e = lane + 64 * j;
+                    if (e < N && !((taken >> j) & 1u) && (key[j] > bk || bi == 0x7fffffff)) {
+                        bk = key[j];
+                        bi = e;
+                    }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const float ok = __shfl_xor(bk, o, kWave);
+                    const int oi = __shfl_xor(bi, o, kWave);
+                    if (oi != 0x7fffffff &&
+                        (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi))) {
+                        bk = ok;
+                        bi = oi;
+                    }
+                }
+                float mine = 0.0f;
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    if (lane + 64 * j == bi) {
+                        taken |= 1u << j;
+                        mine = s32[j];
+                    }
+                sel[k] = bi;
+                sv[k] = __shfl(mine, bi & 63, kWave);
+            }
+        }
+        // ---- gates: s, or s / (double sum of the selected s in k order)
+        double den = 0.0;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            if (k < K) den += (double)sv[k];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            if (k < K && lane == k) {
+                const float g = renorm ? (float)((double)sv[k] / den) : sv[k];
+                idx_out[(size_t)t * K + k] = sel[k];
+                w_out[(size_t)t * K + k] = g;
+                atomicAdd(&hist[sel[k]], 1);
+            }
+        }
+    }
+    // ---- per-block partial sums of s for P_i, combined in a fixed order
+    if (p_partial) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) psum[wave][lane + 64 * j] = pacc[j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        if (hist[e]) atomicAdd(&counts[e], hist[e]);
+        if (p_partial) {
+            double s = psum[0][e];
+            for (int w = 1; w < kSelWaves; ++w) s += psum[w][e];
+            p_partial[(size_t)blockIdx.x * N + e] = s;
+        }
+    }
+}
+
+hipError_t launch_select(const moe_config &c, const float *logits, const float *offset,
+                         const float *bias, int32_t *idx, float *w, int32_t *counts,
+                         double *p_partial, hipStream_t s) {
+    const int J = (c.n_routed + 63) / 64;
+    const int tpb = select_tokens_per_block(c);
+    dim3 grid(select_blocks(c)), block(kSelWaves * kWave);
+#define MOE_SEL(JJ)                                                                            \
+    hipLaunchKernelGGL(k_select<JJ>, grid, block, 0, s, c.T, c.n_routed, c.top_k, c.scoring,   \
+                       c.renorm, tpb, logits, offset, bias, idx, w, counts, p_partial)
+    if (J <= 1) MOE_SEL(1);
+    else if (J <= 2) MOE_SEL(2);
+    else if (J <= 4) MOE_SEL(4);
+    else if (J <= 6) MOE_SEL(6);
+    else if (J <= 8) MOE_SEL(8);
+    else MOE_SEL(16);
+#undef MOE_SEL
+    return hipGetLastError();
+}
+
+// ============================================================ hash routing
+
+// MurmurHash3's 32-bit finaliser (public domain, Austin Appleby).
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+__global__ __launch_bounds__(256) void k_hash_route(int T, int N, const uint32_t *__restrict__ tid,
+                                                    int32_t *__restrict__ idx,
+                                                    float *__restrict__ w,
+                                                    int32_t *__restrict__ counts) {
+    extern __shared__ int32_t hhist[];
+    for (int e = threadIdx.x; e < N; e += blockDim.x) hhist[e] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < T) {
+        const int e = (int)(fmix32(tid[t]) % (uint32_t)N);
+        idx[t] = e;
+        w[t] = 1.0f;
+        atomicAdd(&hhist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x)
+        if (hhist[e]) atomicAdd(&counts[e], hhist[e]);
+}
+
+hipError_t launch_hash_route(const moe_config &c, const uint32_t *tid, int32_t *idx, float *w,
+                             int32_t *counts, hipStream_t s) {
+    hipLaunchKernelGGL(k_hash_route, dim3((c.T + 255) / 256), dim3(256),
+                       (size_t)c.n_routed * sizeof(int32_t), s, c.T, c.n_routed, tid, idx, w,
+                       counts);
+    return hipGetLastError();
+}
+
+// ============================================================ utilities
+
+__global__ void k_fill_i32(int32_t *p, int n, int32_t v) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+// ============================================================ balance stats
+
+// f_i = N' c_i / (K' T); P_i = (1/T) sum over blocks of the partial sums (in
+// block order); loss = alpha1 / N' sum_i f_i P_i (double, fixed tree order).
+__global__ __launch_bounds__(1024) void k_balance(int T, int N, int K, const int32_t *__restrict__ c,
+                                                  const double *__restrict__ part, int nblk,
+                                                  float alpha1, float *__restrict__ f,
+                                                  float *__restrict__ P, float *__restrict__ loss) {
+    __shared__ double red[1024];
+    double acc = 0.0;
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        const double fe = (double)((int64_t)N * c[e]) / (double)((int64_t)K * T);
+        f[e] = (float)fe;
+        if (part) {
+            double s = 0.0;
+            for (int b = 0; b < nblk; ++b) s += part[(size_t)b * N + e];
+            const double pe = s / (double)T;
+            if (P) P[e] = (float)pe;
+            acc += fe * pe;
+        }
+    }
+    if (!loss) return;
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        loss[0] = (float)((double)alpha1 / (double)N * red[0]);
+        loss[1] = (float)red[0];
+    }
+}
+
+hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts,
+                                const double *p_partial, int n_blocks, float alpha1, float *f,
+                                float *P, float *loss, hipStream_t s) {
+    hipLaunchKernelGGL(k_balance, dim3(1), dim3(1024), 0, s, c.T, c.n_routed, c.top_k, counts,
+                       p_partial, n_blocks, alpha1, f, P, loss);
+    return hipGetLastError();
+}
+
+}  // namespace moe

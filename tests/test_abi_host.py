@@ -1,0 +1,158 @@
+"""Host-side checks of libmoe.so that need no GPU: the library loads, exports
+every entry point include/moe.h declares, sizes its workspaces, and rejects
+bad arguments with the documented status codes before touching a device."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from fine_grained_moe_router_amd import binding as B
+from fine_grained_moe_router_amd.configs import CONFIGS
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "moe.h"
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def cfg_of(name, **kw):
+    return B.make_config(CONFIGS[name].with_(**kw) if kw else CONFIGS[name])
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_sizes(L, name):
+    c = cfg_of(name)
+    cfg = CONFIGS[name]
+    fwd = B.workspace_bytes(c, B.WS_FORWARD)
+    P = cfg.T * cfg.top_k
+    # at least the routed hidden activations and the fp32 routed outputs
+    eb = 2 if cfg.dtype == "bf16" else 4
+    assert fwd >= P * cfg.d_ff * eb + P * cfg.d_model * 4
+    if cfg.scoring == "hash":
+        assert B.workspace_bytes(c, B.WS_ROUTE) == 0
+        assert B.workspace_bytes(c, B.WS_PSTAT) == 0
+    else:
+        assert B.workspace_bytes(c, B.WS_ROUTE) >= cfg.T * cfg.n_routed * 4
+        assert B.workspace_bytes(c, B.WS_PSTAT) >= cfg.n_routed * 8
+    assert B.workspace_bytes(c, 99) == 0
+
+
+BAD_CONFIGS = [
+    (dict(T=0), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=65), B.MOE_ERR_INVALID_ARG),          # K' > N'
+    (dict(top_k=17, n_routed=64), B.MOE_ERR_INVALID_ARG),
+    (dict(n_routed=2000), B.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(d_model=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff_shared=80), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, top_k=8), B.MOE_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_CONFIGS)
+def test_bad_configs_are_rejected(L, kw, status):
+    c = cfg_of("toy_fp32", **kw)
+    assert L.moe_workspace_bytes(ctypes.byref(c), B.WS_FORWARD) == 0
+    rc = L.moe_forward(ctypes.byref(c), *([ctypes.c_void_p(256)] * 8), ctypes.c_void_p(256),
+                       1 << 40, None)
+    assert rc == status
+
+
+def test_bad_modes_are_rejected(L):
+    for field, val in (("scoring", 7), ("renorm", 2), ("dtype", 5), ("flags", 8),
+                       ("flags", B.LOGITS_IN | B.LOGITS_OUT)):
+        c = cfg_of("toy_fp32")
+        setattr(c, field, val)
+        assert L.moe_workspace_bytes(ctypes.byref(c), B.WS_FORWARD) == 0, field
+    c = cfg_of("v4_hash")
+    c.top_k = 2
+    assert L.moe_workspace_bytes(ctypes.byref(c), B.WS_FORWARD) == 0
+    assert L.moe_workspace_bytes(None, B.WS_FORWARD) == 0
+
+
+P = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+
+
+def route(L, c, x=P, wg=P, off=None, bias=None, tid=None, logits=None, idx=P, w=P, counts=P,
+          pstat=None, ws=P, ws_bytes=1 << 40):
+    return L.moe_route(ctypes.byref(c), x, wg, off, bias, tid, logits, idx, w, counts, pstat, ws,
+                       ws_bytes, None)
+
+
+def test_route_argument_errors(L):
+    c = cfg_of("v3_decode")
+    assert route(L, c, idx=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, c, w=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, c, counts=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, c, x=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, c, wg=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, c, ws=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, c, ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert route(L, c, logits=P) == B.MOE_ERR_INVALID_ARG      # logits given but no flag
+    cin = cfg_of("v3_decode")
+    cin.flags = B.LOGITS_IN
+    assert route(L, cin, logits=None) == B.MOE_ERR_INVALID_ARG
+    cout = cfg_of("v3_decode")
+    cout.flags = B.LOGITS_OUT
+    assert route(L, cout, logits=None) == B.MOE_ERR_INVALID_ARG
+    h = cfg_of("v4_hash")
+    assert route(L, h, tid=None) == B.MOE_ERR_INVALID_ARG       # hash needs token ids
+    assert route(L, h, tid=P, pstat=P) == B.MOE_ERR_INVALID_ARG  # no P under hash
+
+
+def test_forward_argument_errors(L):
+    c = cfg_of("mid")
+    args = [ctypes.c_void_p(4096 * (i + 1)) for i in range(8)]  # x..h
+    for i in (0, 1, 2, 3, 4, 7):          # x, idx, w, w13, w2, h
+        a = list(args)
+        a[i] = None
+        assert L.moe_forward(ctypes.byref(c), *a, P, 1 << 40, None) == B.MOE_ERR_INVALID_ARG, i
+    for i in (5, 6):                       # shared weights required when K_s > 0
+        a = list(args)
+        a[i] = None
+        assert L.moe_forward(ctypes.byref(c), *a, P, 1 << 40, None) == B.MOE_ERR_INVALID_ARG, i
+    assert L.moe_forward(ctypes.byref(c), *args, None, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(ctypes.byref(c), *args, P, 1024, None) == B.MOE_ERR_WORKSPACE
+    a = list(args)
+    a[7] = a[0]                            # h aliases x
+    assert L.moe_forward(ctypes.byref(c), *a, P, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_stats_argument_errors(L):
+    c = cfg_of("mid")
+    st = L.moe_balance_stats
+    assert st(ctypes.byref(c), None, P, 0.01, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert st(ctypes.byref(c), P, P, 0.01, None, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert st(ctypes.byref(c), P, None, 0.01, P, P, None, None) == B.MOE_ERR_INVALID_ARG
+    assert st(ctypes.byref(c), P, None, 0.01, P, None, P, None) == B.MOE_ERR_INVALID_ARG
+    h = cfg_of("v4_hash")
+    assert st(ctypes.byref(h), P, P, 0.01, P, P, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3):
+        assert B.status_string(s)
+    assert "workspace" in B.status_string(B.MOE_ERR_WORKSPACE)
+    assert B.status_string(12345) == "unknown status"
+    with pytest.raises(B.MoeError):
+        B._check(B.MOE_ERR_INVALID_ARG, "x")

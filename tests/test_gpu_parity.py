@@ -1,0 +1,195 @@
+"""HIP path (through the C ABI) against the CPU oracle, on the same seeded
+input bytes.
+
+* Routing given identical fp32 logits: indices and counts bit-exact, gates
+  within one fp32 ulp, in both directions (GPU logits fed to the oracle, and
+  oracle logits fed to the GPU through MOE_LOGITS_IN).
+* Layer output: each side routes from its own logits; bf16 within max-abs
+  2e-2 / rel-L2 5e-3, fp32 within 1e-4 / 1e-5, near-tie tokens excluded.
+* Balance statistics: f bit-exact, P and the loss to 1e-6 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_moe_router_amd import binding as B
+from fine_grained_moe_router_amd.configs import CONFIGS, scaled
+from fine_grained_moe_router_amd.synth import make_inputs, to_numpy
+from oracle import oracle as O
+
+from parity import (compare_h, gpu_h_as_f64, gpu_layer, host, oracle_h, oracle_route_tokens)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "toy_fp32": CONFIGS["toy_fp32"],
+    "mid_ragged": scaled(CONFIGS["mid"], T=333, d_model=320, d_ff=192),
+    "v3_ragged": scaled(CONFIGS["v3_prefill"], T=700, d_model=512, d_ff=128),
+    "v4_skew_ragged": scaled(CONFIGS["v4_skew"], T=500, d_model=384, d_ff=128),
+    "v4_hash_ragged": scaled(CONFIGS["v4_hash"], T=2000, d_model=256, d_ff=64),
+    "no_shared": scaled(CONFIGS["v3_prefill"], T=257, d_model=256, d_ff=128).with_(n_shared=0),
+    "one_token": scaled(CONFIGS["v3_prefill"], T=1, d_model=256, d_ff=128),
+    "dense_mixture": scaled(CONFIGS["mid"], T=130, d_model=128, d_ff=64).with_(
+        n_routed=8, top_k=8, n_shared=1, d_ff_shared=64),
+    "f32_sigmoid": CONFIGS["toy_fp32"].with_(name="f32_sigmoid", T=200, scoring="sigmoid",
+                                             renorm=True, bias=True),
+}
+
+
+def small_inputs(cfg):
+    inp = make_inputs(cfg, "cpu")
+    for k in ("x", "w_gate", "w13", "w2", "w13s", "w2s", "bias", "offset", "token_ids"):
+        v = getattr(inp, k)
+        if v is not None:
+            setattr(inp, k, v.cuda())
+    return inp
+
+
+def check_routing_identical_logits(cfg, inp, r):
+    """GPU logits -> oracle: same indices, counts, gates (<= 1 ulp), stats."""
+    hashed = cfg.scoring == "hash"
+    if hashed:
+        tid = to_numpy(inp.token_ids).view(np.uint32)
+        idx, gate, s32, _ = O.route(None, cfg.n_routed, 1, "hash", False, token_ids=tid)
+    else:
+        lg = to_numpy(r["logits"])
+        idx, gate, s32, _ = O.route(lg, cfg.n_routed, cfg.top_k, cfg.scoring, cfg.renorm,
+                                    offset=host(inp.offset), bias=host(inp.bias))
+    gidx = to_numpy(r["idx"])
+    np.testing.assert_array_equal(gidx, idx)
+    cnt = O.counts(idx, cfg.n_routed)
+    np.testing.assert_array_equal(to_numpy(r["counts"]), cnt)
+    gw = to_numpy(r["w"])
+    ulps = np.abs(gw - gate) / np.spacing(np.abs(gate))
+    assert ulps.max() <= 1.0, ulps.max()
+    a1 = float(np.float32(cfg.alpha1))
+    f, P, loss = O.balance_stats(cnt, s32, cfg.T, cfg.top_k, a1)
+    np.testing.assert_array_equal(to_numpy(r["f"]), f.astype(np.float32))
+    if not hashed:
+        np.testing.assert_allclose(to_numpy(r["P"]), P, rtol=1e-6, atol=1e-12)
+        np.testing.assert_allclose(to_numpy(r["loss"]), loss, rtol=1e-6)
+    return idx, gate
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_end_to_end(name):
+    cfg = SMALL[name]
+    torch.manual_seed(0)
+    inp = small_inputs(cfg)
+    r = gpu_layer(cfg, inp)
+    check_routing_identical_logits(cfg, inp, r)
+    tokens = np.arange(cfg.T)
+    _, idx, gate, _, gap = oracle_route_tokens(cfg, inp, tokens)
+    h_ref = oracle_h(cfg, inp, tokens, idx, gate)
+    compare_h(cfg, gpu_h_as_f64(r["h"]), h_ref, gap)
+
+
+@pytest.mark.parametrize("name", ["toy_fp32", "v3_ragged", "v4_skew_ragged", "mid_ragged"])
+def test_routing_from_oracle_logits(name):
+    """Oracle logits fed to the GPU (MOE_LOGITS_IN): identical selection."""
+    cfg = SMALL[name]
+    inp = small_inputs(cfg)
+    lg, idx, gate, _, _ = oracle_route_tokens(cfg, inp, np.arange(cfg.T))
+    r = B.route(cfg, logits_in=torch.from_numpy(lg).cuda(), offset=inp.offset, bias=inp.bias)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_numpy(r["idx"]), idx)
+    np.testing.assert_array_equal(to_numpy(r["counts"]), O.counts(idx, cfg.n_routed))
+    ulps = np.abs(to_numpy(r["w"]) - gate) / np.spacing(np.abs(gate))
+    assert ulps.max() <= 1.0
+
+
+def test_forward_is_bitwise_deterministic():
+    cfg = SMALL["v3_ragged"]
+    inp = small_inputs(cfg)
+    r = gpu_layer(cfg, inp)
+    h2 = B.forward(cfg, inp.x, r["idx"], r["w"], inp.w13, inp.w2, inp.w13s, inp.w2s)
+    torch.cuda.synchronize()
+    assert torch.equal(r["h"].view(torch.int16), h2.view(torch.int16))
+
+
+def caller_routing_case(cfg, idx_np, gate_np):
+    inp = small_inputs(cfg)
+    idx = torch.from_numpy(idx_np).cuda()
+    w = torch.from_numpy(gate_np).cuda()
+    h = B.forward(cfg, inp.x, idx, w, inp.w13, inp.w2, inp.w13s, inp.w2s)
+    torch.cuda.synchronize()
+    tokens = np.arange(cfg.T)
+    valid = (idx_np >= 0) & (idx_np < cfg.n_routed)
+    h_ref = oracle_h(cfg, inp, tokens, np.where(valid, idx_np, 0), np.where(valid, gate_np, 0))
+    compare_h(cfg, gpu_h_as_f64(h), h_ref, np.full(cfg.T, np.inf))
+
+
+def test_skewed_and_empty_experts():
+    """Every token on expert 5 (several row tiles), a third also on expert 0,
+    all other experts empty; an out-of-range index contributes nothing."""
+    cfg = scaled(CONFIGS["v3_prefill"], T=300, d_model=256, d_ff=128).with_(top_k=3)
+    rng = np.random.default_rng(1)
+    idx = np.full((cfg.T, 3), -1, np.int32)
+    idx[:, 0] = 5
+    idx[::3, 1] = 0
+    idx[1::7, 2] = cfg.n_routed + 3       # out of range
+    idx[2::5, 2] = 200
+    gate = rng.random((cfg.T, 3)).astype(np.float32)
+    caller_routing_case(cfg, idx, gate)
+
+
+def test_segmentation_identity_on_gpu():
+    """m fine experts (column slices) with the coarse gate reproduce the
+    coarse expert: the GPU layer agrees with itself across the split."""
+    base = scaled(CONFIGS["mid"], T=200, d_model=256, d_ff=256).with_(
+        n_routed=8, top_k=2, n_shared=1, d_ff_shared=64)
+    m = 4
+    fine = base.with_(name="fine", n_routed=32, top_k=8, d_ff=64)
+    inp = small_inputs(base)
+    rng = np.random.default_rng(2)
+    idx = np.stack([rng.choice(8, 2, replace=False) for _ in range(base.T)]).astype(np.int32)
+    gate = rng.random((base.T, 2)).astype(np.float32)
+    hc = B.forward(base, inp.x, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda(),
+                   inp.w13, inp.w2, inp.w13s, inp.w2s)
+    f, fm = base.d_ff, base.d_ff // m
+    w13f = torch.empty((32, 2 * fm, base.d_model), dtype=inp.w13.dtype, device="cuda")
+    w2f = torch.empty((32, base.d_model, fm), dtype=inp.w2.dtype, device="cuda")
+    for e in range(8):
+        for j in range(m):
+            w13f[e * m + j, :fm] = inp.w13[e, j * fm:(j + 1) * fm]
+            w13f[e * m + j, fm:] = inp.w13[e, f + j * fm:f + (j + 1) * fm]
+            w2f[e * m + j] = inp.w2[e, :, j * fm:(j + 1) * fm]
+    idxf = np.array([[e * m + j for e in row for j in range(m)] for row in idx], np.int32)
+    gatef = np.repeat(gate, m, axis=1)
+    hf = B.forward(fine, inp.x, torch.from_numpy(idxf).cuda(), torch.from_numpy(gatef).cuda(),
+                   w13f.contiguous(), w2f.contiguous(), inp.w13s, inp.w2s)
+    torch.cuda.synchronize()
+    h_ref = oracle_h(base, inp, np.arange(base.T), idx, gate)
+    compare_h(base, gpu_h_as_f64(hc), h_ref, np.full(base.T, np.inf))
+    compare_h(base, gpu_h_as_f64(hf), h_ref, np.full(base.T, np.inf))
+
+
+# ---------------------------------------------------------------- full sizes
+
+FULL = ["v3_decode", "mid", "v3_prefill", "v4_skew", "v4_hash"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    """The benchmark's workloads at full size, launched as the benchmark
+    launches them: routing of every token checked bit-exactly on identical
+    logits, the layer output checked on sampled tokens (all of them for the
+    64-token decode batch)."""
+    cfg = CONFIGS[name]
+    print(f"[full-size] {name}: generating inputs", flush=True)
+    inp = make_inputs(cfg, "cuda")
+    print(f"[full-size] {name}: GPU layer", flush=True)
+    r = gpu_layer(cfg, inp)
+    print(f"[full-size] {name}: routing parity", flush=True)
+    check_routing_identical_logits(cfg, inp, r)
+    rng = np.random.default_rng(7)
+    if cfg.T <= 64:
+        tokens = np.arange(cfg.T)
+    else:
+        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 10, replace=False)]))
+    print(f"[full-size] {name}: oracle on {len(tokens)} tokens", flush=True)
+    x_h = host(inp.x)
+    _, idx, gate, _, gap = oracle_route_tokens(cfg, inp, tokens, x_h=x_h)
+    h_ref = oracle_h(cfg, inp, tokens, idx, gate, x_h=x_h)
+    h_gpu = gpu_h_as_f64(r["h"])[tokens]
+    print(f"[full-size] {name}: {compare_h(cfg, h_gpu, h_ref, gap)}", flush=True)

@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Throughput of one DeepSeekMoE layer forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch: moe_route (router
+GEMM, scores, selection bias, top-K', gates, counts), moe_forward
+(permutation, grouped gate/up GEMM + SwiGLU, grouped down GEMM with the shared
+experts folded in, combine + residual) and moe_balance_stats (f_i, P_i,
+L_ExpBal).  Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  `roofline` describes the dominant kernel, timed with
+HIP events recorded by the library around each stage during the timed steps;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload.  Other modes:
+    --pmc-summary DIR   turn two `rocprofv3 --pmc` runs (FETCH_SIZE, then
+                        WRITE_SIZE; their output folders DIR/fetch, DIR/write)
+                        of `bench.py --pmc-run` into a traffic record under
+                        profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+COPY_BYTES = 1 << 30           # calibration copy for the PMC traffic scale
+
+# Dominant kernel per stage name, with the symbol rocprofv3 reports for it.
+KERNEL_OF_STAGE = {"gate_up": "k_gate_up_bf16", "down": "k_down_bf16"}
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record_path(workload: str, stage: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{KERNEL_OF_STAGE.get(stage, stage)}_{workload}.json")
+
+
+def read_traffic(workload: str, stage: str):
+    """HBM bytes per launch of the stage's kernel from the committed PMC
+    record, or None if absent or taken on different kernel sources."""
+    p = traffic_record_path(workload, stage)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v3_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short run for rocprofv3 --pmc: a calibration copy plus a few steps")
+    ap.add_argument("--pmc-summary", default=None)
+    return ap.parse_args(argv)
+
+
+class Layer:
+    """Inputs, outputs and workspaces of one workload, allocated once."""
+
+    def __init__(self, cfg, device="cuda"):
+        import torch
+        from fine_grained_moe_router_amd import binding as B
+        from fine_grained_moe_router_amd.synth import make_inputs
+
+        self.B, self.cfg = B, cfg
+        self.inp = make_inputs(cfg, device)
+        T, N, K = cfg.T, cfg.n_routed, cfg.top_k
+        hashed = cfg.scoring == "hash"
+        c0 = B.make_config(cfg)
+        self.route_out = {
+            "idx": torch.empty((T, K), dtype=torch.int32, device=device),
+            "w": torch.empty((T, K), dtype=torch.float32, device=device),
+            "counts": torch.empty(N, dtype=torch.int32, device=device),
+            "pstat": None if hashed else torch.empty(B.workspace_bytes(c0, B.WS_PSTAT), dtype=torch.uint8, device=device),
+        }
+        self.ws_route = B.alloc_workspace(c0, B.WS_ROUTE, device)
+        self.ws_fwd = B.alloc_workspace(c0, B.WS_FORWARD, device)
+        self.h = torch.empty_like(self.inp.x)
+        self.stats_out = {"f": torch.empty(N, dtype=torch.float32, device=device),
+                          "P": torch.empty(N, dtype=torch.float32, device=device),
+                          "loss": torch.empty(2, dtype=torch.float32, device=device)}
+
+    def step(self):
+        B, cfg, inp = self.B, self.cfg, self.inp
+        hashed = cfg.scoring == "hash"
+        r = B.route(cfg, x=inp.x, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias,
+                    token_ids=inp.token_ids, want_pstat=not hashed, out=self.route_out,
+                    workspace=self.ws_route)
+        B.forward(cfg, inp.x, r["idx"], r["w"], inp.w13, inp.w2, inp.w13s, inp.w2s, h=self.h,
+                  workspace=self.ws_fwd)
+        B.balance_stats(cfg, r["counts"], r["pstat"], want_P=not hashed, want_loss=not hashed,
+                        out=self.stats_out)
+        return r
+
+
+def cpu_baseline(layer, target_s: float):
+    """The CPU oracle (as it stands) on the first S tokens of the same
+    workload: router logits, routing and the layer output, double precision."""
+    import numpy as np
+    from oracle import oracle as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import host, host_experts
+
+    cfg, inp = layer.cfg, layer.inp
+    x_h = host(inp.x)
+    wg_h = host(inp.w_gate)
+    off_h, b_h = host(inp.offset), host(inp.bias)
+    tid_h = None if inp.token_ids is None else host(inp.token_ids).view(np.uint32)
+    w13s, w2s = host(inp.w13s), host(inp.w2s)
+
+    def run(n):
+        """Oracle wall time for tokens 0..n-1 (expert copies to the host are
+        not timed)."""
+        tokens = np.arange(n)
+        t0 = time.perf_counter()
+        if cfg.scoring == "hash":
+            idx, gate, _, _ = O.route(None, cfg.n_routed, 1, "hash", False, token_ids=tid_h[:n])
+        else:
+            lg = O.router_logits(x_h, wg_h, tokens=tokens)
+            idx, gate, _, _ = O.route(lg, cfg.n_routed, cfg.top_k, cfg.scoring, cfg.renorm,
+                                      offset=off_h, bias=b_h)
+        t_route = time.perf_counter() - t0
+        need = np.unique(idx)
+        w13 = host_experts(inp.w13, need)
+        w2 = host_experts(inp.w2, need)
+        idx_full = np.zeros((cfg.T, cfg.top_k), np.int32)
+        gate_full = np.zeros((cfg.T, cfg.top_k), np.float32)
+        idx_full[:n], gate_full[:n] = idx, gate
+        t1 = time.perf_counter()
+        O.forward(x_h, idx_full, gate_full, w13, w2, w13s, w2s, tokens=tokens)
+        return t_route + time.perf_counter() - t1
+
+    probe = max(4, O.threads()) if cfg.d_model >= 4096 else 64
+    dt = run(probe)
+    n = int(max(probe, min(cfg.T, probe * target_s / max(dt, 1e-3))))
+    dt2 = run(n) if n > probe else dt
+    return {"value": n / dt2, "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
+            "sample": f"router logits, routing and layer output of the first {n} of {cfg.T} "
+                      f"tokens ({cfg.name}), double-precision C oracle, {dt2:.1f} s wall"}
+
+
+def pmc_summary(out_dir: str, workload: str, stage: str = "gate_up"):
+    """Combine FETCH_SIZE / WRITE_SIZE counter runs into a traffic record."""
+    from fine_grained_moe_router_amd.configs import CONFIGS
+    kernel = KERNEL_OF_STAGE[stage]
+
+    def load(sub, counter):
+        rows = []
+        for p in glob.glob(os.path.join(out_dir, sub, "**", "*counter_collection.csv"), recursive=True):
+            with open(p) as fh:
+                rows += [r for r in csv.DictReader(fh) if r.get("Counter_Name") == counter]
+        if not rows:
+            raise SystemExit(f"no {counter} rows under {out_dir}/{sub}")
+        by = {}
+        for r in rows:
+            key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+            by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+        return by
+
+    res = {}
+    for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        by = load(sub, counter)
+        copy = [v for (k, _), v in by.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        kern = [v for (k, _), v in by.items() if kernel in k]
+        if not copy or not kern:
+            raise SystemExit(f"{counter}: copy or {kernel} dispatches missing")
+        copy_kib = max(copy)
+        factor = (COPY_BYTES / 1024.0) / copy_kib    # true KiB per counted KiB
+        res[counter] = {"kernel_kib_per_launch": sum(kern) / len(kern), "copy_kib": copy_kib,
+                        "scale": factor, "launches": len(kern)}
+    traffic = sum(res[c]["kernel_kib_per_launch"] * res[c]["scale"] * 1024.0 for c in res)
+    rec = {"kernel": kernel, "workload": workload, "config": CONFIGS[workload].__dict__,
+           "counters": res, "traffic_bytes_per_launch": traffic,
+           "copy_bytes": COPY_BYTES, "source_digest": source_digest(),
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE -d {out_dir}/fetch -- python3 bench.py --pmc-run --workload {workload}",
+               f"rocprofv3 --pmc WRITE_SIZE -d {out_dir}/write -- python3 bench.py --pmc-run --workload {workload}",
+               f"python3 bench.py --pmc-summary {out_dir} --workload {workload}"]}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(traffic_record_path(workload, stage), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({"traffic_bytes_per_launch": traffic, "record": traffic_record_path(workload, stage)}))
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer runs on one GPU's share); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.workload)
+        return 0
+
+    import torch
+    from fine_grained_moe_router_amd import accounting as acc
+    from fine_grained_moe_router_amd import binding as B
+    from fine_grained_moe_router_amd.configs import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()   # fails loudly if the HIP library is not built
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    layer = Layer(cfg)
+    torch.cuda.synchronize()
+
+    if args.pmc_run:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)                    # the calibration copy: COPY_BYTES moved in total
+        for _ in range(2):
+            layer.step()
+        torch.cuda.synchronize()
+        print("[bench] pmc run done", file=sys.stderr, flush=True)
+        return 0
+
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    B.profile_enable(16 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = B.profile_collect()
+    ms = (t1 - t0) * 1000.0 / args.steps
+
+    counts = layer.route_out["counts"].cpu()
+    touched = int((counts > 0).sum())
+    fl = acc.layer_flops(cfg)
+    gf = acc.expert_gemm_flops(cfg)
+    by = acc.layer_bytes(cfg, touched)
+    stage_ms = {k: (v["ms"] / v["launches"] if v["launches"] else 0.0) for k, v in stages.items()}
+    dominant = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    dom_s = stage_ms[dominant] / 1000.0
+    if cfg.dtype == "bf16" and cfg.T >= 1024:
+        achieved = gf[dominant] / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        gb = acc.gemm_bytes(cfg, touched)[dominant]
+        achieved = gb / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = read_traffic(cfg.name, dominant)
+    roof["kernel"] = KERNEL_OF_STAGE[dominant]
+    roof["avg_launch_ms"] = stage_ms[dominant]
+
+    out = {
+        "metric": "MoE-layer tokens/sec on 1 MI355X (V3 shape, T=8192); % MFMA / HBM roofline",
+        "value": cfg.T / (ms / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model,
+                   "n_routed": cfg.n_routed, "top_k": cfg.top_k, "n_shared": cfg.n_shared,
+                   "d_ff": cfg.d_ff, "d_ff_shared": cfg.d_ff_shared, "scoring": cfg.scoring,
+                   "renorm": cfg.renorm, "selection_bias": cfg.bias, "zipf_offset": cfg.zipf_s,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"algorithmic_tflop": fl["total"] / 1e12,
+                  "tflops": fl["total"] / (ms / 1000.0) / 1e12,
+                  "mfma_frac": fl["total"] / (ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS,
+                  "algorithmic_gb": by["total"] / 1e9,
+                  "gbs": by["total"] / (ms / 1000.0) / 1e9,
+                  "experts_touched": touched,
+                  "max_over_mean_load": float(counts.max()) / max(float(counts.float().mean()), 1e-9)},
+        "stages_ms": stage_ms,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

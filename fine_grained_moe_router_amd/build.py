@@ -34,30 +34,32 @@ def sources():
     return sorted(CSRC.glob("*.hip"))
 
 
-def _compile(src: Path) -> Path:
-    obj = BUILD / (src.stem + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)]
+def _compile(src: Path, build_dir: Path = BUILD, defines=()) -> Path:
+    obj = build_dir / (src.stem + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src.name}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> Path:
-    BUILD.mkdir(exist_ok=True)
+def build(verbose: bool = False, out: Path = LIB, defines=()) -> Path:
+    """Compile every source and link `out` (defines: extra -D macros)."""
+    build_dir = BUILD if not defines else BUILD / ("v_" + "_".join(d.replace("=", "") for d in defines))
+    build_dir.mkdir(parents=True, exist_ok=True)
     srcs = sources()
     workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB.with_name(LIB.name + ".tmp")
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+    tmp = out.with_name(out.name + ".tmp")
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

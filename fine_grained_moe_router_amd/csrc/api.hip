@@ -56,7 +56,10 @@ int validate(const moe_config *c) {
     if (c->n_shared > 0 && c->d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
     const long long P = (long long)c->T * c->top_k;
     if (P > (1ll << 22)) return MOE_ERR_UNSUPPORTED;
-    if ((long long)c->T * c->d_model > (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+    // the expert GEMMs address rows with 32-bit element offsets
+    if ((long long)c->T * c->d_model >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+    if (2ll * c->d_ff * c->d_model >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+    if (2ll * c->n_shared * c->d_ff_shared * c->d_model >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

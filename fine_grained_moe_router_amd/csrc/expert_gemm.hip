@@ -19,7 +19,7 @@
 // pieces, one per XCD (block b runs on XCD b % 8), so adjacent tiles share
 // that XCD's L2.  Every block walks a bounded range and exits.
 #include "common.h"
-#include "mfma_tile.h"
+#include "mfma_pipe.h"
 #include "simt_tile.h"
 
 namespace moe {
@@ -41,14 +41,24 @@ struct TileJob {
     bool shared;
 };
 
+#ifndef MOE_TILE_ORDER
+#define MOE_TILE_ORDER 1
+#endif
+
 __device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, int bm) {
     TileJob t;
     t.g = find_group(a.tile_base, a.G, tile);
     const int rel = tile - a.tile_base[t.g];
     const int cnt = a.group_cnt[t.g];
     const int mt = (cnt + bm - 1) / bm;
-    t.j = rel / mt;
+#if MOE_TILE_ORDER == 0
+    t.j = rel / mt;               // row tile fastest: row tiles sharing a weight tile adjacent
     t.i = rel - t.j * mt;
+#else
+    const int nt = (a.tile_base[t.g + 1] - a.tile_base[t.g]) / mt;
+    t.i = rel / nt;               // column tile fastest: column tiles sharing rows adjacent
+    t.j = rel - t.i * nt;
+#endif
     t.row0 = t.i * bm;
     t.nrows = min(bm, cnt - t.row0);
     t.shared = (t.g == a.n_routed);
@@ -75,139 +85,169 @@ __device__ __forceinline__ TileRange tile_range(int total) {
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;
-using GateUpTile = MfmaTile<kBM, kBN, kWM, kWN, true>;
-using DownTile = MfmaTile<kBM, kBN, kWM, kWN, false>;
+// Fragments (of 4) wave row wm must compute for a tile with nrows valid rows.
+__device__ __forceinline__ int wave_frags(int nrows) {
+    const int wm = (threadIdx.x >> 6) & 1;
+    const int nblk = (nrows + 31) >> 5;
+    return min(4, max(0, (nblk - wm + 1) >> 1));
+}
 
-__global__ __launch_bounds__(GateUpTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
-    using Tl = GateUpTile;
-    __shared__ u32x4 As[2 * Tl::LDS_A];
-    __shared__ u32x4 Bs[2 * Tl::LDS_B];
-    const TileRange tr = tile_range(a.tile_base[a.G]);
-    const uint16_t *x = (const uint16_t *)a.x;
-    const int fsum = a.n_shared * a.fs;
-    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
-        const TileJob tj = decode_tile(a, tile, kBM);
-        const int zc0 = tj.j * (kBN / 2);   // first hidden column of the tile
-        const int goff = tj.shared ? 0 : a.group_off[tj.g];
-        const uint16_t *arow[Tl::A_LD];
-        const uint16_t *brow[Tl::B_LD];
+// One gate/up tile whose wave computes NF row fragments.
+template <int NF>
+__device__ __forceinline__ void gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
+                                             const OperandRows &rows, int zc0, int zw,
+                                             size_t rbase) {
+    f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
+    pipe_gemm_nf<true, NF>(lds, rows, a.d, 0, 1, 0, acc);
+    // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
+    // split group the residual z - hi goes, rounded, zw columns further.
+    uint16_t *zout = (uint16_t *)(tj.shared ? a.zs : a.zr);
+    const int split = tj.shared ? a.split_s : a.split_r;
+    const size_t zstride = (size_t)zw * (split ? 2 : 1);
 #pragma unroll
-        for (int l = 0; l < Tl::A_LD; ++l) {
-            const int r = Tl::load_row(threadIdx.x, l);
-            const uint16_t *p = nullptr;
-            if (r < tj.nrows) {
-                const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
-                p = x + (size_t)tok * a.d;
-            }
-            arow[l] = p;
-        }
-        const uint16_t *wbase;
-        int wrow0, wup;
-        if (tj.shared) {
-            const int js = zc0 / a.fs;
-            wbase = (const uint16_t *)a.w13s + (size_t)js * 2 * a.fs * a.d;
-            wrow0 = zc0 - js * a.fs;
-            wup = a.fs;
-        } else {
-            wbase = (const uint16_t *)a.w13 + (size_t)tj.g * 2 * a.f * a.d;
-            wrow0 = zc0;
-            wup = a.f;
-        }
+    for (int i = 0; i < NF; ++i) {
 #pragma unroll
-        for (int l = 0; l < Tl::B_LD; ++l) {
-            const int r = Tl::load_row(threadIdx.x, l);
-            const int wr = (r < kBN / 2) ? wrow0 + r : wup + wrow0 + (r - kBN / 2);
-            brow[l] = wbase + (size_t)wr * a.d;
-        }
-        f32x16 acc[Tl::FM][Tl::FN];
-        Tl::run(arow, brow, a.d, 0, 1, 0, As, Bs, acc);
-        // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for
-        // a split group the residual z - hi goes, rounded, zw columns further.
-        uint16_t *zout = (uint16_t *)(tj.shared ? a.zs : a.zr);
-        const int zw = tj.shared ? fsum : a.f;
-        const int split = tj.shared ? a.split_s : a.split_r;
-        const size_t zstride = (size_t)zw * (split ? 2 : 1);
-        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+        for (int h = 0; h < 2; ++h) {
+            const int tid = opaque_tid();
+            const int col = zc0 + pipe_out_col<true>(tid, h);
+            if (col >= zw) continue;
 #pragma unroll
-        for (int i = 0; i < Tl::FM; ++i)
-#pragma unroll
-            for (int h = 0; h < Tl::FN / 2; ++h) {
-                const int col = zc0 + Tl::out_col(h);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = Tl::out_row(i, r);
-                    if (row < tj.nrows) {
-                        const float ga = acc[i][h][r];
-                        const float up = acc[i][h + Tl::FN / 2][r];
-                        const float z = ga / (1.0f + __expf(-ga)) * up;
-                        const uint16_t hi = f32_to_bf16(z);
-                        uint16_t *dst = zout + (rbase + row) * zstride + col;
-                        dst[0] = hi;
-                        if (split) dst[zw] = f32_to_bf16(z - bf16_to_f32(hi));
-                    }
+            for (int r = 0; r < 16; ++r) {
+                const int row = pipe_out_row(tid, i, r);
+                if (row < tj.nrows) {
+                    const float ga = acc[i][h][r];
+                    const float up = acc[i][h + 2][r];
+                    const float z = ga / (1.0f + __expf(-ga)) * up;
+                    const uint16_t hi = f32_to_bf16(z);
+                    uint16_t *dst = zout + (rbase + row) * zstride + col;
+                    dst[0] = hi;
+                    if (split) dst[zw] = f32_to_bf16(z - bf16_to_f32(hi));
                 }
             }
+            // keep one fragment pair live at a time
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
-__global__ __launch_bounds__(DownTile::NT) void k_down_bf16(const GroupedArgs a) {
-    using Tl = DownTile;
-    __shared__ u32x4 As[2 * Tl::LDS_A];
-    __shared__ u32x4 Bs[2 * Tl::LDS_B];
+__global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
+    using P = PipeTile;
+    __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
     const TileRange tr = tile_range(a.tile_base[a.G]);
     const int fsum = a.n_shared * a.fs;
     for (int tile = tr.first; tile < tr.end; tile += tr.step) {
-        const TileJob tj = decode_tile(a, tile, kBM);
-        const int n0 = tj.j * kBN;
+        const TileJob tj = decode_tile(a, tile, P::BM);
+        const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
+        const int zc0 = tj.j * (P::BN / 2);            // first hidden column of the tile
+        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        OperandRows rows;
+        rows.abase = (const uint16_t *)a.x;
+#pragma unroll
+        for (int l = 0; l < P::A_LD; ++l) {
+            int r = P::load_row(threadIdx.x, l);
+            r = (r < tj.nrows) ? r : 0;   // rows past the end re-read row 0 (discarded)
+            const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
+            rows.aoff[l] = (uint32_t)tok * (uint32_t)a.d;
+        }
+        // B rows: hidden columns zc0 .. zc0+127 of W1 (tile rows 0..127) and
+        // of W3 (tile rows 128..255); the shared group's hidden columns run
+        // across its K_s experts.
+        rows.bbase = tj.shared ? (const uint16_t *)a.w13s
+                               : (const uint16_t *)a.w13 + (size_t)tj.g * 2 * a.f * a.d;
+        const int wwidth = tj.shared ? a.fs : a.f;
+#pragma unroll
+        for (int l = 0; l < P::B_LD; ++l) {
+            const int r = P::load_row(threadIdx.x, l);
+            const bool up = r >= P::BN / 2;
+            int zc = zc0 + (up ? r - P::BN / 2 : r);
+            zc = (zc < zw) ? zc : zw - 1;   // columns past the end: discarded
+            const int js = zc / wwidth, c = zc - js * wwidth;
+            rows.boff[l] = ((uint32_t)js * 2 * wwidth + (up ? wwidth : 0) + c) * (uint32_t)a.d;
+        }
+        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+        switch (wave_frags(tj.nrows)) {
+            case 4: gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase); break;
+            case 3: gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase); break;
+            case 2: gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase); break;
+            case 1: gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase); break;
+            default: gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase); break;
+        }
+    }
+}
+
+// One down-projection tile whose wave computes NF row fragments.
+template <int NF>
+__device__ __forceinline__ void down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
+                                          const OperandRows &rows, int K, int split, int n0,
+                                          size_t rbase) {
+    f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
+    if (tj.shared)
+        pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, acc);
+    else
+        pipe_gemm_nf<false, NF>(lds, rows, K, split ? a.f : 0, 1, 0, acc);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tid = opaque_tid();
+            const int row = pipe_out_row(tid, i, r);
+            if (row >= tj.nrows) continue;
+            float *dst;
+            float gate = 1.0f;
+            if (tj.shared) {
+                dst = a.ys + (size_t)(tj.row0 + row) * a.d;
+            } else {
+                const int pair = a.perm[rbase + row];
+                gate = a.topk_w[pair];
+                dst = a.yr + (size_t)pair * a.d;
+            }
+#pragma unroll
+            for (int j = 0; j < PipeTile::FN; ++j) {
+                const int col = n0 + pipe_out_col<false>(tid, j);
+                if (col < a.d) dst[col] = gate * acc[i][j][r];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(PipeTile::NT) void k_down_bf16(const GroupedArgs a) {
+    using P = PipeTile;
+    __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
+    const TileRange tr = tile_range(a.tile_base[a.G]);
+    const int fsum = a.n_shared * a.fs;
+    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
+        const TileJob tj = decode_tile(a, tile, P::BM);
+        const int n0 = tj.j * P::BN;
         const int goff = tj.shared ? 0 : a.group_off[tj.g];
         // K runs over z, or over (hi, lo) of a split group, reusing W2
         const int split = tj.shared ? a.split_s : a.split_r;
         const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
-        const uint16_t *zin = (const uint16_t *)(tj.shared ? a.zs : a.zr);
         const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
-        const uint16_t *arow[Tl::A_LD];
-        const uint16_t *brow[Tl::B_LD];
+        OperandRows rows;
+        rows.abase = (const uint16_t *)(tj.shared ? a.zs : a.zr) + rbase * K;
 #pragma unroll
-        for (int l = 0; l < Tl::A_LD; ++l) {
-            const int r = Tl::load_row(threadIdx.x, l);
-            arow[l] = (r < tj.nrows) ? zin + (rbase + r) * K : nullptr;
+        for (int l = 0; l < P::A_LD; ++l) {
+            int r = P::load_row(threadIdx.x, l);
+            r = (r < tj.nrows) ? r : 0;
+            rows.aoff[l] = (uint32_t)r * (uint32_t)K;
         }
+        const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
+        rows.bbase = tj.shared ? (const uint16_t *)a.w2s
+                               : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
 #pragma unroll
-        for (int l = 0; l < Tl::B_LD; ++l) {
-            const int n = n0 + Tl::load_row(threadIdx.x, l);
-            const uint16_t *p = nullptr;
-            if (n < a.d)
-                p = tj.shared ? (const uint16_t *)a.w2s + (size_t)n * a.fs
-                              : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f + (size_t)n * a.f;
-            brow[l] = p;
+        for (int l = 0; l < P::B_LD; ++l) {
+            int n = n0 + P::load_row(threadIdx.x, l);
+            n = (n < a.d) ? n : a.d - 1;
+            rows.boff[l] = (uint32_t)n * (uint32_t)wk;
         }
-        f32x16 acc[Tl::FM][Tl::FN];
-        if (tj.shared)
-            Tl::run(arow, brow, K, a.fs, a.n_shared, (size_t)a.d * a.fs, As, Bs, acc);
-        else
-            Tl::run(arow, brow, K, split ? a.f : 0, 1, 0, As, Bs, acc);
-#pragma unroll
-        for (int i = 0; i < Tl::FM; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = Tl::out_row(i, r);
-                if (row >= tj.nrows) continue;
-                float *dst;
-                float gate = 1.0f;
-                if (tj.shared) {
-                    dst = a.ys + (size_t)(tj.row0 + row) * a.d;
-                } else {
-                    const int pair = a.perm[rbase + row];
-                    gate = a.topk_w[pair];
-                    dst = a.yr + (size_t)pair * a.d;
-                }
-#pragma unroll
-                for (int j = 0; j < Tl::FN; ++j) {
-                    const int col = n0 + Tl::out_col(j);
-                    if (col < a.d) dst[col] = gate * acc[i][j][r];
-                }
-            }
+        switch (wave_frags(tj.nrows)) {
+            case 4: down_tile<4>(a, tj, lds, rows, K, split, n0, rbase); break;
+            case 3: down_tile<3>(a, tj, lds, rows, K, split, n0, rbase); break;
+            case 2: down_tile<2>(a, tj, lds, rows, K, split, n0, rbase); break;
+            case 1: down_tile<1>(a, tj, lds, rows, K, split, n0, rbase); break;
+            default: down_tile<0>(a, tj, lds, rows, K, split, n0, rbase); break;
+        }
     }
 }
 
@@ -341,7 +381,7 @@ hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a, hipStream_t
     const TileShape ts = tile_shape(c);
     const long long mt = max_tiles(c, ts.bm1, ts.bz1, c.d_ff, c.n_shared * c.d_ff_shared);
     if (c.dtype == MOE_BF16)
-        hipLaunchKernelGGL(k_gate_up_bf16, dim3(persistent_grid(mt, 2)), dim3(GateUpTile::NT), 0,
+        hipLaunchKernelGGL(k_gate_up_bf16, dim3(persistent_grid(mt, 1)), dim3(PipeTile::NT), 0,
                            s, a);
     else
         hipLaunchKernelGGL(k_gate_up_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a);
@@ -352,7 +392,7 @@ hipError_t launch_down(const moe_config &c, const GroupedArgs &a, hipStream_t s)
     const TileShape ts = tile_shape(c);
     const long long mt = max_tiles(c, ts.bm2, ts.bn2, c.d_model, c.d_model);
     if (c.dtype == MOE_BF16)
-        hipLaunchKernelGGL(k_down_bf16, dim3(persistent_grid(mt, 2)), dim3(DownTile::NT), 0, s,
+        hipLaunchKernelGGL(k_down_bf16, dim3(persistent_grid(mt, 1)), dim3(PipeTile::NT), 0, s,
                            a);
     else
         hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a);

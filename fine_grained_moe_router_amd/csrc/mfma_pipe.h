@@ -1,0 +1,237 @@
+// mfma_pipe.h -- the 256x256 bf16 MFMA tile engine of the grouped expert
+// GEMMs (gfx950).
+//
+// C[256][256] = A[256][K] B[256][K]^T, both operands K-contiguous, fp32
+// accumulation with v_mfma_f32_32x32x16_bf16.  Four waves (one per SIMD),
+// 2 x 2, each owning a 128 x 128 accumulator block (256 accumulator
+// registers per lane): the largest per-wave block, so the fewest LDS and
+// L2 bytes per MFMA.
+//
+// Memory pipeline.  k-tiles of 64 values: each row contributes one whole
+// 128-byte cache line per k-tile (half-line requests halve the per-CU rate
+// of L2 hits).  Global data goes straight into LDS with 16-byte
+// global_load_lds (no register staging); a lane's LDS slot is fixed by its
+// lane id, so the swizzle is applied by choosing which global chunk each
+// lane fetches.  LDS row = 128 bytes = 8 chunks of 16 bytes; chunk c of row
+// r sits in slot c ^ ((r >> 1) & 7), so the 16 lanes that read one chunk
+// column of 16 consecutive rows hit 16 distinct 16-byte groups of the
+// 64-bank LDS.
+//
+// The two operands get different depths: B (expert weights, streamed from
+// HBM once, long latency) has three 32 KB stages -- its loads run two
+// k-tiles ahead -- while A (token rows, shared by the column tiles that run
+// together on one XCD and mostly served by L2) has two.  2 x 32 + 3 x 32 KB
+// is the whole 160 KB LDS.  The next k-tile's loads are spread through the
+// MFMA stream (one per group of four MFMAs), so a busy load queue never
+// holds a run of MFMAs back.
+//
+// Partial row tiles: wave row wm owns the 32-row fragments 2 i + wm
+// (i < 4), so a tile with n valid rows issues MFMAs only for fragments that
+// hold a valid row -- the work of a partial tile scales with ceil(n / 64).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct PipeTile {
+    static constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+    static constexpr int A_STAGES = 2, B_STAGES = 3;
+    static constexpr int CHUNKS = BK / 8;                  // 16-byte chunks per row
+    static constexpr int A_LD = BM * CHUNKS / NT;          // global_load_lds per thread, A
+    static constexpr int B_LD = BN * CHUNKS / NT;          // and B
+    static constexpr int A_STAGE = BM * CHUNKS * 16;       // bytes
+    static constexpr int B_STAGE = BN * CHUNKS * 16;
+    static constexpr int LDS_BYTES = A_STAGES * A_STAGE + B_STAGES * B_STAGE;
+    static constexpr int FM = 4, FN = 4;                   // 32x32 fragments per wave
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+    __device__ static __forceinline__ int slot(int row, int chunk) {
+        return chunk ^ ((row >> 1) & 7);
+    }
+    // Row of the tile that load n of thread tid fills; the global chunk it
+    // fetches is the same for every n.
+    __device__ static __forceinline__ int load_row(int tid, int n) {
+        return tid / CHUNKS + n * (NT / CHUNKS);
+    }
+    __device__ static __forceinline__ int load_chunk(int tid) {
+        return slot(load_row(tid, 0), tid % CHUNKS);   // slot() is its own inverse
+    }
+    // B tile row feeding fragment j of wave column wn.  SPLIT: fragments
+    // 0,1 come from the first half (rows wn*64 + 32 j), 2,3 from the second
+    // half at the same offsets.
+    template <bool SPLIT>
+    __device__ static __forceinline__ int b_row(int wn, int j) {
+        if (SPLIT) return (j < 2) ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32;
+        return wn * 128 + j * 32;
+    }
+    // Tile row of fragment i of wave row wm.
+    __device__ static __forceinline__ int a_row(int wm, int i) { return (2 * i + wm) * 32; }
+};
+
+// Row addresses of the rows one thread fetches: a uniform base plus 32-bit
+// element offsets (keeps the per-thread state small).
+struct OperandRows {
+    const uint16_t *abase, *bbase;
+    uint32_t aoff[PipeTile::A_LD];
+    uint32_t boff[PipeTile::B_LD];
+};
+
+// Workgroup barrier without a memory fence.  __syncthreads() would also wait
+// for every outstanding global_load_lds (vmcnt(0)), which drains the load
+// pipeline; here each thread first waits for exactly the loads it needs
+// (wait_vmcnt), and the barrier then makes them visible to all waves.  The
+// signal fences stop the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): own LDS reads/writes done
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void load_lds16(const uint16_t *src, char *lds_dst) {
+    __builtin_amdgcn_global_load_lds((const void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+
+// Run the K loop of one tile.  Every row a thread fetches must be
+// dereferenceable (rows past the valid count point at a valid row; their
+// products are discarded).  NF: how many of this wave's row fragments hold
+// a valid row (0..4) -- all waves run the same loads and barriers, a wave
+// with fewer valid fragments issues fewer MFMAs.  B's k offset of k-tile k0
+// is k0, or ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several
+// matrices side by side along K, possibly repeated).
+template <bool SPLIT, int NF>
+__device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows, int K, int bsplit,
+                                             int bmod, size_t bstride,
+                                             f32x16 (&acc)[NF > 0 ? NF : 1][PipeTile::FN]) {
+    using P = PipeTile;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    const int ca = P::load_chunk(tid) * 8;
+    char *const a_lds = lds;
+    char *const b_lds = lds + P::A_STAGES * P::A_STAGE;
+#pragma unroll
+    for (int i = 0; i < (NF > 0 ? NF : 1); ++i)
+#pragma unroll
+        for (int j = 0; j < P::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto koff_of = [&](int k0) -> size_t {
+        return (bsplit > 0) ? (size_t)((k0 / bsplit) % bmod) * bstride + (size_t)(k0 % bsplit)
+                            : (size_t)k0;
+    };
+    auto a_load = [&](int n, int kt, int stage) {
+        load_lds16(rows.abase + rows.aoff[n] + kt * P::BK + ca,
+                   a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
+    };
+    auto b_load = [&](int n, size_t koff, int stage) {
+        load_lds16(rows.bbase + rows.boff[n] + koff + ca,
+                   b_lds + stage * P::B_STAGE + (n * P::NT + wave * 64) * 16);
+    };
+    const int nk = K / P::BK;
+    // Prologue: A(0), B(0), B(1).  Every iteration kt then issues A(kt+1)
+    // followed by B(kt+2) (clamped to the last k-tile: trailing refetches
+    // land in a stage nobody reads any more).  So at the top of iteration kt
+    // the only loads issued after A(kt) and B(kt) are the B_LD loads of
+    // B(kt+1): vmcnt <= B_LD means both operands of k-tile kt have landed
+    // (vector memory loads complete in order).
+#pragma unroll
+    for (int n = 0; n < P::A_LD; ++n) a_load(n, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const size_t ko = koff_of(min(s, nk - 1) * P::BK);
+#pragma unroll
+        for (int n = 0; n < P::B_LD; ++n) b_load(n, ko, s);
+    }
+    constexpr int SUB = P::BK / 16;          // MFMA k-substeps per k-tile
+    constexpr int SLOTS = 4 * SUB;           // MFMA groups per k-tile
+    constexpr int LOADS = P::A_LD + P::B_LD;
+    static_assert(LOADS % SLOTS == 0, "load interleave");
+    constexpr int PER_SLOT = LOADS / SLOTS;
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<P::B_LD>();   // A(kt) and B(kt) have landed (this thread's share)
+        lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
+        const int ka = min(kt + 1, nk - 1);
+        const size_t kbo = koff_of(min(kt + 2, nk - 1) * P::BK);
+        const int sa_next = (kt + 1) % P::A_STAGES;
+        const int sb_next = (kt + 2) % P::B_STAGES;
+        const u32x4 *Ab = (const u32x4 *)(a_lds + (kt % P::A_STAGES) * P::A_STAGE);
+        const u32x4 *Bb = (const u32x4 *)(b_lds + (kt % P::B_STAGES) * P::B_STAGE);
+        bf16x8 a[2][NF > 0 ? NF : 1], b[2][P::FN];
+        auto frag_load = [&](int s, bf16x8 (&av)[NF > 0 ? NF : 1], bf16x8 (&bv)[P::FN]) {
+            const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+            for (int j = 0; j < P::FN; ++j) {
+                const int row = P::b_row<SPLIT>(wn, j) + (lane & 31);
+                bv[j] = __builtin_bit_cast(bf16x8, Bb[row * P::CHUNKS + P::slot(row, ch)]);
+            }
+#pragma unroll
+            for (int i = 0; i < NF; ++i) {
+                const int row = P::a_row(wm, i) + (lane & 31);
+                av[i] = __builtin_bit_cast(bf16x8, Ab[row * P::CHUNKS + P::slot(row, ch)]);
+            }
+        };
+        frag_load(0, a[0], b[0]);
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            if (s + 1 < SUB) frag_load(s + 1, a[(s + 1) & 1], b[(s + 1) & 1]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int i = 0; i < NF; ++i)
+                    if (i == q)
+#pragma unroll
+                        for (int j = 0; j < P::FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < PER_SLOT; ++u) {
+                    const int n = (s * 4 + q) * PER_SLOT + u;   // A loads first, then B
+                    if (n < P::A_LD) a_load(n, ka, sa_next);
+                    else b_load(n - P::A_LD, kbo, sb_next);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    wait_vmcnt<0>();   // trailing refetches land before the LDS is reused
+    lds_barrier();     // every wave done with the stages before the LDS is reused
+}
+
+// Thread id the compiler cannot treat as loop-invariant: epilogue address
+// arithmetic stays next to its use instead of being hoisted out of the
+// persistent tile loop (where 64 precomputed offsets would spill).
+__device__ __forceinline__ int opaque_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// Output coordinates of accumulator register r of fragment (i, j), given
+// tid = opaque_tid().
+__device__ __forceinline__ int pipe_out_row(int tid, int i, int r) {
+    const int lane = tid & 63;
+    const int wm = (tid >> 6) & 1;
+    return PipeTile::a_row(wm, i) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+// SPLIT: column within a half (fragment j < 2); else column of the tile.
+template <bool SPLIT>
+__device__ __forceinline__ int pipe_out_col(int tid, int j) {
+    const int lane = tid & 63;
+    const int wn = (tid >> 6) >> 1;
+    return (SPLIT ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+}
+
+}  // namespace moe

@@ -19,7 +19,7 @@ static int perm_chunk(int pairs) {
 }
 
 TileShape tile_shape(const moe_config &c) {
-    if (c.dtype == MOE_BF16) return TileShape{128, 64, 128, 128};
+    if (c.dtype == MOE_BF16) return TileShape{256, 128, 256, 256};
     return TileShape{64, 32, 64, 64};
 }
 
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
         const int c = cnt[g];
         const int width = (g < N) ? f : fsum;
-        t1[g] = ((c + ts.bm1 - 1) / ts.bm1) * (width / ts.bz1);
+        t1[g] = ((c + ts.bm1 - 1) / ts.bm1) * ((width + ts.bz1 - 1) / ts.bz1);
         t2[g] = ((c + ts.bm2 - 1) / ts.bm2) * ntn2;
         meta[mi.group_cnt + g] = c;
     }

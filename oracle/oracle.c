@@ -48,6 +48,7 @@
  *    only to build skewed workloads).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -89,6 +90,9 @@ void oracle_router_logits(int64_t n_tok, const int64_t *tokens, int64_t d,
         }
     }
 }
+
+/* Threads the OpenMP loops of this oracle use. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* MurmurHash3's 32-bit finaliser (public domain, Austin Appleby). */
 uint32_t oracle_fmix32(uint32_t h)

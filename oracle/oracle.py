@@ -63,6 +63,8 @@ def _load():
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     lib.oracle_router_logits.argtypes = [i64, vp, i64, i64, i32, vp, vp, vp]
     lib.oracle_router_logits.restype = None
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = i32
     lib.oracle_fmix32.argtypes = [ctypes.c_uint32]
     lib.oracle_fmix32.restype = ctypes.c_uint32
     lib.oracle_route.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -95,6 +97,11 @@ def _c(a, dtype=None):
         return None
     a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
     return a
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def fmix32(v: int) -> int:

@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-COPY_BYTES = 1 << 30           # calibration copy for the PMC traffic scale
+COPY_BYTES = 1 << 30           # calibration copy: reads COPY_BYTES/2, writes COPY_BYTES/2
 
 # Dominant kernel per stage name, with the symbol rocprofv3 reports for it.
 KERNEL_OF_STAGE = {"gate_up": "k_gate_up_bf16", "down": "k_down_bf16"}
@@ -193,7 +193,7 @@ def pmc_summary(out_dir: str, workload: str, stage: str = "gate_up"):
         if not copy or not kern:
             raise SystemExit(f"{counter}: copy or {kernel} dispatches missing")
         copy_kib = max(copy)
-        factor = (COPY_BYTES / 1024.0) / copy_kib    # true KiB per counted KiB
+        factor = (COPY_BYTES / 2 / 1024.0) / copy_kib    # true KiB per counted KiB
         res[counter] = {"kernel_kib_per_launch": sum(kern) / len(kern), "copy_kib": copy_kib,
                         "scale": factor, "launches": len(kern)}
     traffic = sum(res[c]["kernel_kib_per_launch"] * res[c]["scale"] * 1024.0 for c in res)

@@ -74,7 +74,7 @@ def oracle_h(cfg: LayerConfig, inp: LayerInputs, tokens, idx_t, gate_t, x_h=None
 
 
 def compare_h(cfg: LayerConfig, h_gpu: np.ndarray, h_ref: np.ndarray, gap: np.ndarray):
-    """Assert the benchmark spec's tolerance on tokens whose gap is not a near tie.
+    """Assert the end-to-end tolerance on tokens whose gap is not a near tie.
     Returns (max_abs, rel_l2, n_excluded)."""
     tol = TOL[cfg.dtype]
     keep = gap >= tol["gap"]

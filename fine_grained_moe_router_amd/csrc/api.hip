@@ -145,7 +145,7 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     hipError_t e;
     {
         StageScope sc(MOE_STAGE_PERMUTE, s);
-        if ((e = launch_permute(c, L, topk_idx, ws, s)) != hipSuccess) return hip_fail(e);
+        if ((e = launch_permute(c, L, topk_idx, topk_w, ws, s)) != hipSuccess) return hip_fail(e);
     }
     const MetaIdx mi = meta_index(L.G);
     const int32_t *meta = (const int32_t *)(ws + L.off_meta);
@@ -162,8 +162,11 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     a.split_s = z_split_shared(c) ? 1 : 0;
     a.group_off = meta + mi.group_off;
     a.group_cnt = meta + mi.group_cnt;
+    a.mt_base = meta + mi.mt;
+    a.gang = 1;
+    a.nt_routed = a.nt_shared = 1;
     a.perm = (const int32_t *)(ws + L.off_perm);
-    a.topk_w = topk_w;
+    a.gsort = (const float *)(ws + L.off_gsort);
     a.x = x;
     a.w13 = w13;
     a.w2 = w2;
@@ -176,11 +179,13 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     {
         StageScope sc(MOE_STAGE_GATE_UP, s);
         a.tile_base = meta + mi.tile1;
+        a.xsplit = meta + mi.xs1;
         if ((e = launch_gate_up(c, a, s)) != hipSuccess) return hip_fail(e);
     }
     {
         StageScope sc(MOE_STAGE_DOWN, s);
         a.tile_base = meta + mi.tile2;
+        a.xsplit = meta + mi.xs2;
         if ((e = launch_down(c, a, s)) != hipSuccess) return hip_fail(e);
     }
     {

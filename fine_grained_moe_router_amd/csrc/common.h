@@ -51,6 +51,7 @@ struct FwdLayout {
     size_t off_chunk;   // int32 [n_chunks][N']: per-chunk counts, then bases
     size_t off_meta;    // int32 meta block (see MetaIdx)
     size_t off_perm;    // int32 [T*K']: pair id at each expert-ordered row
+    size_t off_gsort;   // fp32 [T*K']: gate of each expert-ordered row
     size_t off_zr;      // [T*K'][d_ff] dtype: routed hidden activations
     size_t off_zs;      // [T][K_s*d_ff_shared] dtype: shared hidden activations
     size_t off_yr;      // fp32 [T*K'][d]: gate-scaled routed outputs, pair order
@@ -59,8 +60,13 @@ struct FwdLayout {
 };
 
 // Offsets (in int32 elements) of the arrays inside the meta block.
+//   group_off[G+1], group_cnt[G+1]   rows of each group
+//   tile1[G+1], tile2[G+1]           tile prefix sums of the two GEMMs
+//   mt[G+1]                          row-tile prefix sums (256-row tiles)
+//   xs1[9], xs2[9]                   per-XCD row-tile ranges of the two GEMMs
+//   bad                              count of out-of-range expert ids
 struct MetaIdx {
-    int group_off, group_cnt, tile1, tile2, bad, size;
+    int group_off, group_cnt, tile1, tile2, mt, xs1, xs2, bad, size;
 };
 __host__ __device__ inline MetaIdx meta_index(int G) {
     MetaIdx m;
@@ -68,8 +74,11 @@ __host__ __device__ inline MetaIdx meta_index(int G) {
     m.group_cnt = G + 1;
     m.tile1 = 2 * G + 2;
     m.tile2 = 3 * G + 3;
-    m.bad = 4 * G + 4;
-    m.size = 4 * G + 8;
+    m.mt = 4 * G + 4;
+    m.xs1 = 5 * G + 5;
+    m.xs2 = 5 * G + 14;
+    m.bad = 5 * G + 23;
+    m.size = 5 * G + 24;
     return m;
 }
 
@@ -84,8 +93,12 @@ struct GroupedArgs {
     int T, d, top_k, n_routed, n_shared, f, fs, G;
     int split_r, split_s;     // hidden activation carried as a bf16 (hi, lo) pair
     const int32_t *group_off, *group_cnt, *tile_base;
+    // gang schedule of the bf16 kernels: row-tile prefix sums, per-XCD
+    // row-tile ranges, gang size, column tiles per row tile
+    const int32_t *mt_base, *xsplit;
+    int gang, nt_routed, nt_shared;
     const int32_t *perm;      // pair id per expert-ordered row
-    const float *topk_w;      // [T*K']
+    const float *gsort;       // gate per expert-ordered row
     const void *x, *w13, *w2, *w13s, *w2s;
     void *zr, *zs;
     float *yr, *ys;
@@ -116,7 +129,7 @@ inline bool z_split_routed(const moe_config &c) { return c.dtype == MOE_BF16 && 
 FwdLayout fwd_layout(const moe_config &c);
 TileShape tile_shape(const moe_config &c);
 hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t *idx,
-                          char *ws, hipStream_t s);
+                          const float *topk_w, char *ws, hipStream_t s);
 hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a, hipStream_t s);
 hipError_t launch_down(const moe_config &c, const GroupedArgs &a, hipStream_t s);
 hipError_t launch_combine(const moe_config &c, const void *x, const int32_t *idx,

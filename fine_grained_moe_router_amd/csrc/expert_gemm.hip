@@ -130,61 +130,121 @@ __device__ __forceinline__ void gate_up_tile(const GroupedArgs &a, const TileJob
     }
 }
 
-__global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
+// Gang schedule of the bf16 kernels.  The blocks of one XCD form gangs of
+// a.gang blocks; a gang takes whole row tiles of the XCD's row-tile range
+// (a.xsplit, balanced by cost), and gang member s computes column tiles
+// s, s + a.gang, ... of each.  The members of a gang therefore do identical
+// work on the same token rows at the same time, so those rows are fetched
+// from HBM once and then served by the XCD's L2.
+struct Gang {
+    int m, end, step, member, size;
+};
+
+__device__ __forceinline__ bool gang_of(const GroupedArgs &a, Gang &g) {
+    const int xcd = blockIdx.x % kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int nslots = gridDim.x / kXcds;
+    const int ngang = nslots / a.gang;
+    const int gang = slot / a.gang;
+    if (gang >= ngang) return false;   // left-over blocks of the XCD stay idle
+    g.member = slot - gang * a.gang;
+    g.m = a.xsplit[xcd] + gang;
+    g.end = a.xsplit[xcd + 1];
+    g.step = ngang;
+    g.size = a.gang;
+    return true;
+}
+
+__device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm) {
+    TileJob t;
+    t.g = find_group(a.mt_base, a.G, m);
+    t.i = m - a.mt_base[t.g];
+    t.j = 0;
+    t.row0 = t.i * bm;
+    t.nrows = min(bm, a.group_cnt[t.g] - t.row0);
+    t.shared = (t.g == a.n_routed);
+    return t;
+}
+
+__device__ __forceinline__ void gate_up_body(const GroupedArgs &a, const TileJob &tj, char *lds) {
     using P = PipeTile;
-    __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
-    const TileRange tr = tile_range(a.tile_base[a.G]);
     const int fsum = a.n_shared * a.fs;
-    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
-        const TileJob tj = decode_tile(a, tile, P::BM);
-        const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
-        const int zc0 = tj.j * (P::BN / 2);            // first hidden column of the tile
-        const int goff = tj.shared ? 0 : a.group_off[tj.g];
-        OperandRows rows;
-        rows.abase = (const uint16_t *)a.x;
+    const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
+    const int zc0 = tj.j * (P::BN / 2);            // first hidden column of the tile
+    const int goff = tj.shared ? 0 : a.group_off[tj.g];
+    OperandRows rows;
+    rows.abase = (const uint16_t *)a.x;
 #pragma unroll
-        for (int l = 0; l < P::A_LD; ++l) {
-            int r = P::load_row(threadIdx.x, l);
-            r = (r < tj.nrows) ? r : 0;   // rows past the end re-read row 0 (discarded)
-            const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
-            rows.aoff[l] = (uint32_t)tok * (uint32_t)a.d;
-        }
-        // B rows: hidden columns zc0 .. zc0+127 of W1 (tile rows 0..127) and
-        // of W3 (tile rows 128..255); the shared group's hidden columns run
-        // across its K_s experts.
-        rows.bbase = tj.shared ? (const uint16_t *)a.w13s
-                               : (const uint16_t *)a.w13 + (size_t)tj.g * 2 * a.f * a.d;
-        const int wwidth = tj.shared ? a.fs : a.f;
+    for (int l = 0; l < P::A_LD; ++l) {
+        int r = P::load_row(threadIdx.x, l);
+        r = (r < tj.nrows) ? r : 0;   // rows past the end re-read row 0 (discarded)
+        const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
+        rows.aoff[l] = (uint32_t)tok * (uint32_t)a.d;
+    }
+    // B rows: hidden columns zc0 .. zc0+127 of W1 (tile rows 0..127) and of
+    // W3 (tile rows 128..255); the shared group's hidden columns run across
+    // its K_s experts.
+    rows.bbase = tj.shared ? (const uint16_t *)a.w13s
+                           : (const uint16_t *)a.w13 + (size_t)tj.g * 2 * a.f * a.d;
+    const int wwidth = tj.shared ? a.fs : a.f;
 #pragma unroll
-        for (int l = 0; l < P::B_LD; ++l) {
-            const int r = P::load_row(threadIdx.x, l);
-            const bool up = r >= P::BN / 2;
-            int zc = zc0 + (up ? r - P::BN / 2 : r);
-            zc = (zc < zw) ? zc : zw - 1;   // columns past the end: discarded
-            const int js = zc / wwidth, c = zc - js * wwidth;
-            rows.boff[l] = ((uint32_t)js * 2 * wwidth + (up ? wwidth : 0) + c) * (uint32_t)a.d;
-        }
-        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
-        switch (wave_frags(tj.nrows)) {
-            case 4: gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase); break;
-            case 3: gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase); break;
-            case 2: gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase); break;
-            case 1: gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase); break;
-            default: gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase); break;
+    for (int l = 0; l < P::B_LD; ++l) {
+        const int r = P::load_row(threadIdx.x, l);
+        const bool up = r >= P::BN / 2;
+        int zc = zc0 + (up ? r - P::BN / 2 : r);
+        zc = (zc < zw) ? zc : zw - 1;   // columns past the end: discarded
+        const int js = zc / wwidth, c = zc - js * wwidth;
+        rows.boff[l] = ((uint32_t)js * 2 * wwidth + (up ? wwidth : 0) + c) * (uint32_t)a.d;
+    }
+    const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+    switch (wave_frags(tj.nrows)) {
+        case 4: gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase); break;
+        case 3: gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase); break;
+        case 2: gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase); break;
+        case 1: gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase); break;
+        default: gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase); break;
+    }
+}
+
+__global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
+    Gang gang;
+    if (!gang_of(a, gang)) return;
+    for (int m = gang.m; m < gang.end; m += gang.step) {
+        TileJob tj = row_tile(a, m, PipeTile::BM);
+        const int nt = tj.shared ? a.nt_shared : a.nt_routed;
+        for (int j = gang.member; j < nt; j += gang.size) {
+            tj.j = j;
+            gate_up_body(a, tj, lds);
         }
     }
 }
 
 // One down-projection tile whose wave computes NF row fragments.
+// (pair, gate) of row t of a routed tile sits in LDS word pair t of the
+// epilogue area: the third B stage, which no wave reads after the K loop and
+// which the next tile first writes after the top barrier of its first k-tile.
+constexpr int kRowInfoOffset = PipeTile::A_STAGES * PipeTile::A_STAGE + 2 * PipeTile::B_STAGE;
+static_assert(PipeTile::NT == PipeTile::BM, "one tile row per thread");
+static_assert(PipeTile::B_STAGES == 3, "row info lives in the third B stage");
+
+// One down-projection tile whose wave computes NF row fragments.  Thread t
+// brings the pair id and gate of tile row t (fetched before the K loop); the
+// epilogue reads them back from LDS, so its stores never wait on a load.
 template <int NF>
 __device__ __forceinline__ void down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                           const OperandRows &rows, int K, int split, int n0,
-                                          size_t rbase) {
+                                          int my_pair, float my_gate) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
     if (tj.shared)
         pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, acc);
     else
         pipe_gemm_nf<false, NF>(lds, rows, K, split ? a.f : 0, 1, 0, acc);
+    int2 *info = (int2 *)(lds + kRowInfoOffset);
+    if (!tj.shared) {
+        info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
+        lds_barrier();
+    }
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
 #pragma unroll
@@ -197,9 +257,9 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, const TileJob &t
             if (tj.shared) {
                 dst = a.ys + (size_t)(tj.row0 + row) * a.d;
             } else {
-                const int pair = a.perm[rbase + row];
-                gate = a.topk_w[pair];
-                dst = a.yr + (size_t)pair * a.d;
+                const int2 v = info[row];
+                gate = __int_as_float(v.y);
+                dst = a.yr + (size_t)v.x * a.d;
             }
 #pragma unroll
             for (int j = 0; j < PipeTile::FN; ++j) {
@@ -211,42 +271,57 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, const TileJob &t
     }
 }
 
-__global__ __launch_bounds__(PipeTile::NT) void k_down_bf16(const GroupedArgs a) {
+__device__ __forceinline__ void down_body(const GroupedArgs &a, const TileJob &tj, char *lds) {
     using P = PipeTile;
-    __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
-    const TileRange tr = tile_range(a.tile_base[a.G]);
     const int fsum = a.n_shared * a.fs;
-    for (int tile = tr.first; tile < tr.end; tile += tr.step) {
-        const TileJob tj = decode_tile(a, tile, P::BM);
-        const int n0 = tj.j * P::BN;
-        const int goff = tj.shared ? 0 : a.group_off[tj.g];
-        // K runs over z, or over (hi, lo) of a split group, reusing W2
-        const int split = tj.shared ? a.split_s : a.split_r;
-        const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
-        const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
-        OperandRows rows;
-        rows.abase = (const uint16_t *)(tj.shared ? a.zs : a.zr) + rbase * K;
+    const int n0 = tj.j * P::BN;
+    const int goff = tj.shared ? 0 : a.group_off[tj.g];
+    // K runs over z, or over (hi, lo) of a split group, reusing W2
+    const int split = tj.shared ? a.split_s : a.split_r;
+    const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
+    const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+    OperandRows rows;
+    rows.abase = (const uint16_t *)(tj.shared ? a.zs : a.zr) + rbase * K;
 #pragma unroll
-        for (int l = 0; l < P::A_LD; ++l) {
-            int r = P::load_row(threadIdx.x, l);
-            r = (r < tj.nrows) ? r : 0;
-            rows.aoff[l] = (uint32_t)r * (uint32_t)K;
-        }
-        const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
-        rows.bbase = tj.shared ? (const uint16_t *)a.w2s
-                               : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
+    for (int l = 0; l < P::A_LD; ++l) {
+        int r = P::load_row(threadIdx.x, l);
+        r = (r < tj.nrows) ? r : 0;
+        rows.aoff[l] = (uint32_t)r * (uint32_t)K;
+    }
+    const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
+    rows.bbase = tj.shared ? (const uint16_t *)a.w2s
+                           : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
 #pragma unroll
-        for (int l = 0; l < P::B_LD; ++l) {
-            int n = n0 + P::load_row(threadIdx.x, l);
-            n = (n < a.d) ? n : a.d - 1;
-            rows.boff[l] = (uint32_t)n * (uint32_t)wk;
-        }
-        switch (wave_frags(tj.nrows)) {
-            case 4: down_tile<4>(a, tj, lds, rows, K, split, n0, rbase); break;
-            case 3: down_tile<3>(a, tj, lds, rows, K, split, n0, rbase); break;
-            case 2: down_tile<2>(a, tj, lds, rows, K, split, n0, rbase); break;
-            case 1: down_tile<1>(a, tj, lds, rows, K, split, n0, rbase); break;
-            default: down_tile<0>(a, tj, lds, rows, K, split, n0, rbase); break;
+    for (int l = 0; l < P::B_LD; ++l) {
+        int n = n0 + P::load_row(threadIdx.x, l);
+        n = (n < a.d) ? n : a.d - 1;
+        rows.boff[l] = (uint32_t)n * (uint32_t)wk;
+    }
+    int my_pair = 0;
+    float my_gate = 0.0f;
+    if (!tj.shared && (int)threadIdx.x < tj.nrows) {
+        my_pair = a.perm[rbase + threadIdx.x];
+        my_gate = a.gsort[rbase + threadIdx.x];
+    }
+    switch (wave_frags(tj.nrows)) {
+        case 4: down_tile<4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
+        case 3: down_tile<3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
+        case 2: down_tile<2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
+        case 1: down_tile<1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
+        default: down_tile<0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
+    }
+}
+
+__global__ __launch_bounds__(PipeTile::NT) void k_down_bf16(const GroupedArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
+    Gang gang;
+    if (!gang_of(a, gang)) return;
+    for (int m = gang.m; m < gang.end; m += gang.step) {
+        TileJob tj = row_tile(a, m, PipeTile::BM);
+        const int nt = tj.shared ? a.nt_shared : a.nt_routed;
+        for (int j = gang.member; j < nt; j += gang.size) {
+            tj.j = j;
+            down_body(a, tj, lds);
         }
     }
 }
@@ -332,7 +407,7 @@ __global__ __launch_bounds__(256) void k_down_f32(const GroupedArgs a) {
                 dst = a.ys + (size_t)(tj.row0 + row) * a.d;
             } else {
                 const int pair = a.perm[rbase + row];
-                gate = a.topk_w[pair];
+                gate = a.gsort[rbase + row];
                 dst = a.yr + (size_t)pair * a.d;
             }
 #pragma unroll
@@ -377,25 +452,42 @@ static long long max_tiles(const moe_config &c, int bm, int ncols_tile, int widt
     return n;
 }
 
-hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a, hipStream_t s) {
+// Gang size for a GEMM whose row tiles have nt column tiles: one pass per
+// row tile when nt fits in an XCD's blocks, else the fewest equal passes.
+static int gang_size(int nt, int nslots) {
+    if (nt <= nslots) return nt;
+    const int passes = (nt + nslots - 1) / nslots;
+    return (nt + passes - 1) / passes;
+}
+
+hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a0, hipStream_t s) {
     const TileShape ts = tile_shape(c);
     const long long mt = max_tiles(c, ts.bm1, ts.bz1, c.d_ff, c.n_shared * c.d_ff_shared);
-    if (c.dtype == MOE_BF16)
-        hipLaunchKernelGGL(k_gate_up_bf16, dim3(persistent_grid(mt, 1)), dim3(PipeTile::NT), 0,
-                           s, a);
+    if (c.dtype == MOE_BF16) {
+        const int grid = persistent_grid(1ll << 30, 1);
+        GroupedArgs a = a0;
+        a.nt_routed = (c.d_ff + ts.bz1 - 1) / ts.bz1;
+        a.nt_shared = (c.n_shared * c.d_ff_shared + ts.bz1 - 1) / ts.bz1;
+        a.gang = gang_size(a.nt_routed, grid / kXcds);
+        hipLaunchKernelGGL(k_gate_up_bf16, dim3(grid), dim3(PipeTile::NT), 0, s, a);
+    }
     else
-        hipLaunchKernelGGL(k_gate_up_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_gate_up_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a0);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const moe_config &c, const GroupedArgs &a, hipStream_t s) {
+hipError_t launch_down(const moe_config &c, const GroupedArgs &a0, hipStream_t s) {
     const TileShape ts = tile_shape(c);
     const long long mt = max_tiles(c, ts.bm2, ts.bn2, c.d_model, c.d_model);
-    if (c.dtype == MOE_BF16)
-        hipLaunchKernelGGL(k_down_bf16, dim3(persistent_grid(mt, 1)), dim3(PipeTile::NT), 0, s,
-                           a);
-    else
-        hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a);
+    if (c.dtype == MOE_BF16) {
+        const int grid = persistent_grid(1ll << 30, 1);
+        GroupedArgs a = a0;
+        a.nt_routed = a.nt_shared = (c.d_model + ts.bn2 - 1) / ts.bn2;
+        a.gang = gang_size(a.nt_routed, grid / kXcds);
+        hipLaunchKernelGGL(k_down_bf16, dim3(grid), dim3(PipeTile::NT), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a0);
+    }
     return hipGetLastError();
 }
 

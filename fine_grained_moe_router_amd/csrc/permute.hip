@@ -39,6 +39,8 @@ FwdLayout fwd_layout(const moe_config &c) {
     o = align256(o + (size_t)meta_index(L.G).size * 4);
     L.off_perm = o;
     o = align256(o + P * 4);
+    L.off_gsort = o;
+    o = align256(o + P * 4);
     L.off_zr = o;
     o = align256(o + P * c.d_ff * eb * (z_split_routed(c) ? 2 : 1));
     L.off_zs = o;
@@ -95,13 +97,55 @@ __device__ int block_excl_scan(int32_t *data, int n, int32_t *tmp) {
     return total;
 }
 
+// Per-XCD row-tile ranges of one GEMM, balanced by estimated cost: a row
+// tile with r valid rows costs nt (2 + ceil(r / 64)) (nt column tiles, each
+// streaming its weight tile and issuing MFMAs for ceil(r / 64) 64-row
+// slices).  Row tile m of group g starts at cost gcost_base[g] + i nt 6 (all
+// but a group's last row tile are full).  XCD x takes the row tiles whose
+// start cost lies in [x C / 8, (x + 1) C / 8).
+__device__ void xcd_splits(int G, const int32_t *cnt, const int32_t *mtb, const int32_t *ntg,
+                           int32_t *gcost, int32_t *tmp, int32_t *out) {
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+        const int mt = mtb[g + 1] - mtb[g];
+        gcost[g] = ntg[g] * (2 * mt + (cnt[g] + 63) / 64);
+    }
+    __syncthreads();
+    const int C = block_excl_scan(gcost, G, tmp);   // gcost now holds the group start costs
+    const int M = mtb[G];
+    if (threadIdx.x <= 8) out[threadIdx.x] = (threadIdx.x == 0) ? 0 : M;
+    __syncthreads();
+    for (int m = threadIdx.x; m < M; m += blockDim.x) {
+        int lo = 0, hi = G;   // mtb[lo] <= m < mtb[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (mtb[mid] <= m) lo = mid;
+            else hi = mid;
+        }
+        const long long start = gcost[lo] + (long long)(m - mtb[lo]) * ntg[lo] * 6;
+        long long prev = -1;
+        if (m > 0) {
+            const int pm = m - 1;
+            int plo = (mtb[lo] <= pm) ? lo : lo - 1;
+            while (plo > 0 && mtb[plo] > pm) --plo;
+            prev = gcost[plo] + (long long)(pm - mtb[plo]) * ntg[plo] * 6;
+        }
+        for (int x = 1; x < 8; ++x) {
+            const long long target = (long long)x * C / 8;
+            if (start >= target && prev < target) out[x] = m;
+        }
+    }
+    __syncthreads();
+}
+
 // One block.  Turns chunk counts into chunk bases (relative to the expert),
-// computes group row counts/offsets and the tile prefix sums of both GEMMs.
+// computes group row counts/offsets, the tile prefix sums of both GEMMs, the
+// row-tile prefix sums and the per-XCD row-tile ranges.
 __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, int n_shared,
                                                     int f, int fsum, int d, TileShape ts,
                                                     int32_t *__restrict__ cc,
                                                     int32_t *__restrict__ meta) {
     __shared__ int32_t cnt[2048], t1[2048], t2[2048], tmp[1024];
+    __shared__ int32_t mtb[2048], nt1[2048], nt2[2048], gcost[2048];
     const int G = N + (n_shared > 0 ? 1 : 0);
     const MetaIdx mi = meta_index(G);
     for (int e = threadIdx.x; e < 2048; e += blockDim.x) {
@@ -125,13 +169,22 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
         const int c = cnt[g];
         const int width = (g < N) ? f : fsum;
-        t1[g] = ((c + ts.bm1 - 1) / ts.bm1) * ((width + ts.bz1 - 1) / ts.bz1);
+        nt1[g] = (width + ts.bz1 - 1) / ts.bz1;
+        nt2[g] = ntn2;
+        t1[g] = ((c + ts.bm1 - 1) / ts.bm1) * nt1[g];
         t2[g] = ((c + ts.bm2 - 1) / ts.bm2) * ntn2;
+        mtb[g] = (c + ts.bm1 - 1) / ts.bm1;
         meta[mi.group_cnt + g] = c;
     }
     __syncthreads();
     const int tot1 = block_excl_scan(t1, G, tmp);
     const int tot2 = block_excl_scan(t2, G, tmp);
+    const int totm = block_excl_scan(mtb, G, tmp);
+    if (threadIdx.x == 0) mtb[G] = totm;
+    __syncthreads();
+    for (int g = threadIdx.x; g <= G; g += blockDim.x) meta[mi.mt + g] = mtb[g];
+    xcd_splits(G, cnt, mtb, nt1, gcost, tmp, meta + mi.xs1);
+    xcd_splits(G, cnt, mtb, nt2, gcost, tmp, meta + mi.xs2);
     // row offsets of the routed groups (the shared group reads rows 0..T-1)
     if (threadIdx.x == 0 && n_shared > 0) cnt[N] = 0;
     __syncthreads();
@@ -148,12 +201,14 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
 }
 
 // Stable placement: thread e scans its chunk's ids in pair order and writes
-// every pair that chose e to the next row of expert e.
+// every pair that chose e (and its gate) to the next row of expert e.
 __global__ __launch_bounds__(256) void k_perm_scatter(int P, int N, int chunk,
                                                       const int32_t *__restrict__ idx,
+                                                      const float *__restrict__ topk_w,
                                                       const int32_t *__restrict__ cc,
                                                       const int32_t *__restrict__ group_off,
-                                                      int32_t *__restrict__ perm) {
+                                                      int32_t *__restrict__ perm,
+                                                      float *__restrict__ gsort) {
     extern __shared__ int32_t ids[];
     const int p0 = blockIdx.x * chunk, n = min(P, p0 + chunk) - p0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) ids[i] = idx[p0 + i];
@@ -161,12 +216,15 @@ __global__ __launch_bounds__(256) void k_perm_scatter(int P, int N, int chunk,
     for (int e = threadIdx.x; e < N; e += blockDim.x) {
         int pos = group_off[e] + cc[(size_t)blockIdx.x * N + e];
         for (int i = 0; i < n; ++i)
-            if (ids[i] == e) perm[pos++] = p0 + i;
+            if (ids[i] == e) {
+                perm[pos] = p0 + i;
+                gsort[pos++] = topk_w[p0 + i];
+            }
     }
 }
 
-hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t *idx, char *ws,
-                          hipStream_t s) {
+hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t *idx,
+                          const float *topk_w, char *ws, hipStream_t s) {
     const int P = c.T * c.top_k;
     const int N = c.n_routed;
     int32_t *cc = (int32_t *)(ws + L.off_chunk);
@@ -179,7 +237,8 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, L.n_chunks, c.T, c.n_shared,
                        c.d_ff, c.n_shared * c.d_ff_shared, c.d_model, tile_shape(c), cc, meta);
     hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
-                       L.chunk, idx, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm));
+                       L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
+                       (float *)(ws + L.off_gsort));
     return hipGetLastError();
 }
 

@@ -163,7 +163,6 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     a.group_off = meta + mi.group_off;
     a.group_cnt = meta + mi.group_cnt;
     a.mt_base = meta + mi.mt;
-    a.gang = 1;
     a.nt_routed = a.nt_shared = 1;
     a.perm = (const int32_t *)(ws + L.off_perm);
     a.gsort = (const float *)(ws + L.off_gsort);
@@ -180,12 +179,14 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
         StageScope sc(MOE_STAGE_GATE_UP, s);
         a.tile_base = meta + mi.tile1;
         a.xsplit = meta + mi.xs1;
+        a.queue = (int32_t *)meta + mi.q1;
         if ((e = launch_gate_up(c, a, s)) != hipSuccess) return hip_fail(e);
     }
     {
         StageScope sc(MOE_STAGE_DOWN, s);
         a.tile_base = meta + mi.tile2;
         a.xsplit = meta + mi.xs2;
+        a.queue = (int32_t *)meta + mi.q2;
         if ((e = launch_down(c, a, s)) != hipSuccess) return hip_fail(e);
     }
     {

@@ -64,9 +64,11 @@ struct FwdLayout {
 //   tile1[G+1], tile2[G+1]           tile prefix sums of the two GEMMs
 //   mt[G+1]                          row-tile prefix sums (256-row tiles)
 //   xs1[9], xs2[9]                   per-XCD row-tile ranges of the two GEMMs
+//   q1[8], q2[8]                     per-XCD work counters of the two GEMMs
 //   bad                              count of out-of-range expert ids
+// q1, q2 and bad start at zero (set by the permutation).
 struct MetaIdx {
-    int group_off, group_cnt, tile1, tile2, mt, xs1, xs2, bad, size;
+    int group_off, group_cnt, tile1, tile2, mt, xs1, xs2, q1, q2, bad, size;
 };
 __host__ __device__ inline MetaIdx meta_index(int G) {
     MetaIdx m;
@@ -77,8 +79,10 @@ __host__ __device__ inline MetaIdx meta_index(int G) {
     m.mt = 4 * G + 4;
     m.xs1 = 5 * G + 5;
     m.xs2 = 5 * G + 14;
-    m.bad = 5 * G + 23;
-    m.size = 5 * G + 24;
+    m.q1 = 5 * G + 23;
+    m.q2 = 5 * G + 31;
+    m.bad = 5 * G + 39;
+    m.size = 5 * G + 40;
     return m;
 }
 
@@ -93,10 +97,11 @@ struct GroupedArgs {
     int T, d, top_k, n_routed, n_shared, f, fs, G;
     int split_r, split_s;     // hidden activation carried as a bf16 (hi, lo) pair
     const int32_t *group_off, *group_cnt, *tile_base;
-    // gang schedule of the bf16 kernels: row-tile prefix sums, per-XCD
-    // row-tile ranges, gang size, column tiles per row tile
+    // work queues of the bf16 kernels: row-tile prefix sums, per-XCD
+    // row-tile ranges and item counters, column tiles per row tile
     const int32_t *mt_base, *xsplit;
-    int gang, nt_routed, nt_shared;
+    int32_t *queue;
+    int nt_routed, nt_shared;
     const int32_t *perm;      // pair id per expert-ordered row
     const float *gsort;       // gate per expert-ordered row
     const void *x, *w13, *w2, *w13s, *w2s;

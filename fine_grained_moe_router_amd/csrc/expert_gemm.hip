@@ -85,6 +85,15 @@ __device__ __forceinline__ TileRange tile_range(int total) {
 
 // ---------------------------------------------------------------- bf16 MFMA
 
+// Bit n set when A load n of this thread fetches one of the nrows valid rows.
+__device__ __forceinline__ uint32_t valid_row_mask(int nrows) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int n = 0; n < PipeTile::A_LD; ++n)
+        m |= (PipeTile::load_row(threadIdx.x, n) < nrows ? 1u : 0u) << n;
+    return m;
+}
+
 // Fragments (of 4) wave row wm must compute for a tile with nrows valid rows.
 __device__ __forceinline__ int wave_frags(int nrows) {
     const int wm = (threadIdx.x >> 6) & 1;
@@ -92,13 +101,92 @@ __device__ __forceinline__ int wave_frags(int nrows) {
     return min(4, max(0, (nblk - wm + 1) >> 1));
 }
 
+// Work queue of the bf16 kernels.  XCD x owns the row tiles
+// [xsplit[x], xsplit[x+1]) (balanced by cost); its work items are the
+// (row tile, column tile) pairs of that range.  The blocks of the XCD pull
+// items in order from the XCD's counter, so the blocks busy at any moment
+// hold consecutive items and share their operands through the XCD's L2;
+// pulling also balances tiles of unequal cost.  Item order within a group:
+// a routed expert with at most kColMajorRows row tiles in the range lists
+// them row tile fastest -- its row tiles that stream the same weight tile
+// start together -- while a longer group (the shared experts, a heavily
+// loaded expert) lists column tile fastest, so the gang of column tiles on
+// one row tile shares its token rows.
+constexpr int kColMajorRows = 4;
+
+struct XcdQueue {
+    int m0, ms, m1, ntr, nts, nr_items, total;
+    int32_t *ctr;
+};
+__device__ __forceinline__ XcdQueue xcd_queue(const GroupedArgs &a) {
+    const int x = blockIdx.x % kXcds;
+    XcdQueue q;
+    q.m0 = a.xsplit[x];
+    q.m1 = a.xsplit[x + 1];
+    // the shared group (if any) is the last group: its row tiles come last
+    const int first_shared = a.mt_base[a.n_routed];
+    q.ms = min(max(first_shared, q.m0), q.m1);
+    q.ntr = a.nt_routed;
+    q.nts = a.nt_shared;
+    q.nr_items = (q.ms - q.m0) * q.ntr;
+    q.total = q.nr_items + (q.m1 - q.ms) * q.nts;
+    q.ctr = a.queue + x;
+    return q;
+}
+// Item -> (row tile m, column tile j).  The routed items of a group with
+// rows lo .. lo + r - 1 of the range are items (lo - m0) nt ... + r nt - 1.
+__device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue &q, int item,
+                                           int &m, int &j) {
+    int lo, r, local, nt;
+    if (item < q.nr_items) {
+        nt = q.ntr;
+        const int g = find_group(a.mt_base, a.n_routed, q.m0 + item / nt);
+        lo = max(a.mt_base[g], q.m0);
+        r = min(a.mt_base[g + 1], q.ms) - lo;
+        local = item - (lo - q.m0) * nt;
+    } else {
+        nt = q.nts;
+        lo = q.ms;
+        r = q.m1 - q.ms;
+        local = item - q.nr_items;
+    }
+    if (item < q.nr_items && r <= kColMajorRows) {
+        j = local / r;
+        m = lo + (local - j * r);
+    } else {
+        const int i = local / nt;
+        m = lo + i;
+        j = local - i * nt;
+    }
+}
+
+// The item a block works on next is pulled by thread 0 when a tile starts
+// and handed to the other threads through one LDS word in the second A
+// stage: after the K loop no wave reads that stage, and the next tile first
+// writes it after the top barrier of its first k-tile, which every wave
+// reaches only after it has read the word.
+constexpr int kQueueSlotOffset = PipeTile::A_STAGE;
+static_assert(PipeTile::A_STAGES == 2, "queue slot lives in the second A stage");
+
+__device__ __forceinline__ int pull_item(int32_t *ctr) {
+    return (threadIdx.x == 0) ? atomicAdd(ctr, 1) : 0;
+}
+// Called by every thread right after the K loop of a tile.
+__device__ __forceinline__ int publish_item(char *lds, int next) {
+    int32_t *slot = (int32_t *)(lds + kQueueSlotOffset);
+    if (threadIdx.x == 0) *slot = next;
+    lds_barrier();
+    return __builtin_amdgcn_readfirstlane(*slot);
+}
+
 // One gate/up tile whose wave computes NF row fragments.
 template <int NF>
-__device__ __forceinline__ void gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                             const OperandRows &rows, int zc0, int zw,
-                                             size_t rbase) {
+__device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
+                                            const OperandRows &rows, int zc0, int zw,
+                                            size_t rbase, int next) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
     pipe_gemm_nf<true, NF>(lds, rows, a.d, 0, 1, 0, acc);
+    const int item = publish_item(lds, next);
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
     // split group the residual z - hi goes, rounded, zw columns further.
     uint16_t *zout = (uint16_t *)(tj.shared ? a.zs : a.zr);
@@ -128,31 +216,7 @@ __device__ __forceinline__ void gate_up_tile(const GroupedArgs &a, const TileJob
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-}
-
-// Gang schedule of the bf16 kernels.  The blocks of one XCD form gangs of
-// a.gang blocks; a gang takes whole row tiles of the XCD's row-tile range
-// (a.xsplit, balanced by cost), and gang member s computes column tiles
-// s, s + a.gang, ... of each.  The members of a gang therefore do identical
-// work on the same token rows at the same time, so those rows are fetched
-// from HBM once and then served by the XCD's L2.
-struct Gang {
-    int m, end, step, member, size;
-};
-
-__device__ __forceinline__ bool gang_of(const GroupedArgs &a, Gang &g) {
-    const int xcd = blockIdx.x % kXcds;
-    const int slot = blockIdx.x / kXcds;
-    const int nslots = gridDim.x / kXcds;
-    const int ngang = nslots / a.gang;
-    const int gang = slot / a.gang;
-    if (gang >= ngang) return false;   // left-over blocks of the XCD stay idle
-    g.member = slot - gang * a.gang;
-    g.m = a.xsplit[xcd] + gang;
-    g.end = a.xsplit[xcd + 1];
-    g.step = ngang;
-    g.size = a.gang;
-    return true;
+    return item;
 }
 
 __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm) {
@@ -166,7 +230,8 @@ __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm)
     return t;
 }
 
-__device__ __forceinline__ void gate_up_body(const GroupedArgs &a, const TileJob &tj, char *lds) {
+__device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob &tj, char *lds,
+                                            int next) {
     using P = PipeTile;
     const int fsum = a.n_shared * a.fs;
     const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
@@ -177,10 +242,11 @@ __device__ __forceinline__ void gate_up_body(const GroupedArgs &a, const TileJob
 #pragma unroll
     for (int l = 0; l < P::A_LD; ++l) {
         int r = P::load_row(threadIdx.x, l);
-        r = (r < tj.nrows) ? r : 0;   // rows past the end re-read row 0 (discarded)
+        r = (r < tj.nrows) ? r : 0;   // rows past the end are not fetched
         const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
         rows.aoff[l] = (uint32_t)tok * (uint32_t)a.d;
     }
+    rows.amask = valid_row_mask(tj.nrows);
     // B rows: hidden columns zc0 .. zc0+127 of W1 (tile rows 0..127) and of
     // W3 (tile rows 128..255); the shared group's hidden columns run across
     // its K_s experts.
@@ -198,25 +264,25 @@ __device__ __forceinline__ void gate_up_body(const GroupedArgs &a, const TileJob
     }
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
     switch (wave_frags(tj.nrows)) {
-        case 4: gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase); break;
-        case 3: gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase); break;
-        case 2: gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase); break;
-        case 1: gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase); break;
-        default: gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase); break;
+        case 4: return gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase, next);
+        case 3: return gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase, next);
+        case 2: return gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase, next);
+        case 1: return gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase, next);
+        default: return gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase, next);
     }
 }
 
 __global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
-    Gang gang;
-    if (!gang_of(a, gang)) return;
-    for (int m = gang.m; m < gang.end; m += gang.step) {
+    const XcdQueue q = xcd_queue(a);
+    int item = publish_item(lds, pull_item(q.ctr));
+    while (item < q.total) {
+        const int next = pull_item(q.ctr);
+        int m, j;
+        queue_item(a, q, item, m, j);
         TileJob tj = row_tile(a, m, PipeTile::BM);
-        const int nt = tj.shared ? a.nt_shared : a.nt_routed;
-        for (int j = gang.member; j < nt; j += gang.size) {
-            tj.j = j;
-            gate_up_body(a, tj, lds);
-        }
+        tj.j = j;
+        item = gate_up_body(a, tj, lds, next);
     }
 }
 
@@ -232,19 +298,17 @@ static_assert(PipeTile::B_STAGES == 3, "row info lives in the third B stage");
 // brings the pair id and gate of tile row t (fetched before the K loop); the
 // epilogue reads them back from LDS, so its stores never wait on a load.
 template <int NF>
-__device__ __forceinline__ void down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                          const OperandRows &rows, int K, int split, int n0,
-                                          int my_pair, float my_gate) {
+__device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
+                                         const OperandRows &rows, int K, int split, int n0,
+                                         int my_pair, float my_gate, int next) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
     if (tj.shared)
         pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, acc);
     else
         pipe_gemm_nf<false, NF>(lds, rows, K, split ? a.f : 0, 1, 0, acc);
     int2 *info = (int2 *)(lds + kRowInfoOffset);
-    if (!tj.shared) {
-        info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
-        lds_barrier();
-    }
+    if (!tj.shared) info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
+    const int item = publish_item(lds, next);   // its barrier also publishes info
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
 #pragma unroll
@@ -269,9 +333,11 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, const TileJob &t
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    return item;
 }
 
-__device__ __forceinline__ void down_body(const GroupedArgs &a, const TileJob &tj, char *lds) {
+__device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj, char *lds,
+                                         int next) {
     using P = PipeTile;
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
@@ -288,6 +354,7 @@ __device__ __forceinline__ void down_body(const GroupedArgs &a, const TileJob &t
         r = (r < tj.nrows) ? r : 0;
         rows.aoff[l] = (uint32_t)r * (uint32_t)K;
     }
+    rows.amask = valid_row_mask(tj.nrows);
     const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
     rows.bbase = tj.shared ? (const uint16_t *)a.w2s
                            : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
@@ -304,25 +371,25 @@ __device__ __forceinline__ void down_body(const GroupedArgs &a, const TileJob &t
         my_gate = a.gsort[rbase + threadIdx.x];
     }
     switch (wave_frags(tj.nrows)) {
-        case 4: down_tile<4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
-        case 3: down_tile<3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
-        case 2: down_tile<2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
-        case 1: down_tile<1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
-        default: down_tile<0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate); break;
+        case 4: return down_tile<4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
+        case 3: return down_tile<3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
+        case 2: return down_tile<2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
+        case 1: return down_tile<1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
+        default: return down_tile<0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
     }
 }
 
 __global__ __launch_bounds__(PipeTile::NT) void k_down_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
-    Gang gang;
-    if (!gang_of(a, gang)) return;
-    for (int m = gang.m; m < gang.end; m += gang.step) {
+    const XcdQueue q = xcd_queue(a);
+    int item = publish_item(lds, pull_item(q.ctr));
+    while (item < q.total) {
+        const int next = pull_item(q.ctr);
+        int m, j;
+        queue_item(a, q, item, m, j);
         TileJob tj = row_tile(a, m, PipeTile::BM);
-        const int nt = tj.shared ? a.nt_shared : a.nt_routed;
-        for (int j = gang.member; j < nt; j += gang.size) {
-            tj.j = j;
-            down_body(a, tj, lds);
-        }
+        tj.j = j;
+        item = down_body(a, tj, lds, next);
     }
 }
 
@@ -452,14 +519,6 @@ static long long max_tiles(const moe_config &c, int bm, int ncols_tile, int widt
     return n;
 }
 
-// Gang size for a GEMM whose row tiles have nt column tiles: one pass per
-// row tile when nt fits in an XCD's blocks, else the fewest equal passes.
-static int gang_size(int nt, int nslots) {
-    if (nt <= nslots) return nt;
-    const int passes = (nt + nslots - 1) / nslots;
-    return (nt + passes - 1) / passes;
-}
-
 hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a0, hipStream_t s) {
     const TileShape ts = tile_shape(c);
     const long long mt = max_tiles(c, ts.bm1, ts.bz1, c.d_ff, c.n_shared * c.d_ff_shared);
@@ -468,7 +527,6 @@ hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a0, hipStream_
         GroupedArgs a = a0;
         a.nt_routed = (c.d_ff + ts.bz1 - 1) / ts.bz1;
         a.nt_shared = (c.n_shared * c.d_ff_shared + ts.bz1 - 1) / ts.bz1;
-        a.gang = gang_size(a.nt_routed, grid / kXcds);
         hipLaunchKernelGGL(k_gate_up_bf16, dim3(grid), dim3(PipeTile::NT), 0, s, a);
     }
     else
@@ -483,7 +541,6 @@ hipError_t launch_down(const moe_config &c, const GroupedArgs &a0, hipStream_t s
         const int grid = persistent_grid(1ll << 30, 1);
         GroupedArgs a = a0;
         a.nt_routed = a.nt_shared = (c.d_model + ts.bn2 - 1) / ts.bn2;
-        a.gang = gang_size(a.nt_routed, grid / kXcds);
         hipLaunchKernelGGL(k_down_bf16, dim3(grid), dim3(PipeTile::NT), 0, s, a);
     } else {
         hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a0);

@@ -75,6 +75,7 @@ struct OperandRows {
     const uint16_t *abase, *bbase;
     uint32_t aoff[PipeTile::A_LD];
     uint32_t boff[PipeTile::B_LD];
+    uint32_t amask;   // bit n: A load n fetches a valid row (the rest are skipped)
 };
 
 // Workgroup barrier without a memory fence.  __syncthreads() would also wait
@@ -101,9 +102,9 @@ __device__ __forceinline__ void load_lds16(const uint16_t *src, char *lds_dst) {
                                      (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
 
-// Run the K loop of one tile.  Every row a thread fetches must be
-// dereferenceable (rows past the valid count point at a valid row; their
-// products are discarded).  NF: how many of this wave's row fragments hold
+// Run the K loop of one tile.  A rows past the valid count are not fetched
+// (rows.amask): their LDS rows keep stale values, which only reach output
+// rows that are discarded.  Every B row must be dereferenceable.  NF: how many of this wave's row fragments hold
 // a valid row (0..4) -- all waves run the same loads and barriers, a wave
 // with fewer valid fragments issues fewer MFMAs.  B's k offset of k-tile k0
 // is k0, or ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several
@@ -133,8 +134,9 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
                             : (size_t)k0;
     };
     auto a_load = [&](int n, int kt, int stage) {
-        load_lds16(rows.abase + rows.aoff[n] + kt * P::BK + ca,
-                   a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
+        if ((rows.amask >> n) & 1)
+            load_lds16(rows.abase + rows.aoff[n] + kt * P::BK + ca,
+                       a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
     };
     auto b_load = [&](int n, size_t koff, int stage) {
         load_lds16(rows.bbase + rows.boff[n] + koff + ca,

@@ -230,7 +230,7 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
     int32_t *cc = (int32_t *)(ws + L.off_chunk);
     int32_t *meta = (int32_t *)(ws + L.off_meta);
     const MetaIdx mi = meta_index(L.G);
-    hipError_t e = launch_fill_i32(meta + mi.bad, 1, 0, s);
+    hipError_t e = launch_fill_i32(meta + mi.q1, mi.bad + 1 - mi.q1, 0, s);   // q1, q2, bad
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_perm_hist, dim3(L.n_chunks), dim3(256), (size_t)N * 4, s, P, N, L.chunk,
                        idx, cc, meta + mi.bad);

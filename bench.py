@@ -41,11 +41,17 @@ COPY_BYTES = 1 << 30           # calibration copy: reads COPY_BYTES/2, writes CO
 KERNEL_OF_STAGE = {"gate_up": "k_gate_up_bf16", "down": "k_down_bf16"}
 
 
+# Sources that decide what the grouped GEMM kernels do (their code, their
+# work lists and their launch arguments): a traffic record is valid for the
+# kernel only while these are unchanged.
+GEMM_SOURCES = ("common.h", "mfma_pipe.h", "expert_gemm.hip", "permute.hip", "api.hip")
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", "*"))):
-        with open(p, "rb") as fh:
-            h.update(os.path.basename(p).encode())
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -56,7 +62,7 @@ def traffic_record_path(workload: str, stage: str) -> str:
 
 def read_traffic(workload: str, stage: str):
     """HBM bytes per launch of the stage's kernel from the committed PMC
-    record, or None if absent or taken on different kernel sources."""
+    record, or None if absent or taken on different GEMM sources."""
     p = traffic_record_path(workload, stage)
     if not os.path.exists(p):
         return None

@@ -63,9 +63,16 @@ int validate(const moe_config *c) {
     return MOE_OK;
 }
 
+// Route workspace: [T][N'] fp32 logits (used unless the caller passes its
+// own logits buffer), then [splits][T][N'] fp32 partial sums of a split
+// router GEMM.
+size_t route_logits_bytes(const moe_config &c) {
+    return ((size_t)c.T * c.n_routed * sizeof(float) + 255) & ~(size_t)255;
+}
 size_t route_ws(const moe_config &c) {
     if (c.scoring == MOE_ROUTE_HASH) return 0;
-    return ((size_t)c.T * c.n_routed * sizeof(float) + 255) & ~(size_t)255;
+    const int z = router_splits(c);
+    return route_logits_bytes(c) * (z > 1 ? 1 + z : 1);
 }
 
 size_t pstat_bytes(const moe_config &c) {
@@ -112,14 +119,16 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const fl
         if (!x || !w_gate) return MOE_ERR_INVALID_ARG;
         if (c.flags & MOE_LOGITS_OUT) {
             if (!logits) return MOE_ERR_INVALID_ARG;
-        } else {
-            if (logits) return MOE_ERR_INVALID_ARG;
-            if (!workspace) return MOE_ERR_INVALID_ARG;
-            if (ws_bytes < route_ws(c)) return MOE_ERR_WORKSPACE;
-            lg = (float *)workspace;
+        } else if (logits) {
+            return MOE_ERR_INVALID_ARG;
         }
+        if (!workspace) return MOE_ERR_INVALID_ARG;
+        if (ws_bytes < route_ws(c)) return MOE_ERR_WORKSPACE;
+        if (!(c.flags & MOE_LOGITS_OUT)) lg = (float *)workspace;
+        float *part = (float *)((char *)workspace + route_logits_bytes(c));
         StageScope sc(MOE_STAGE_ROUTER_GEMM, s);
-        if ((e = launch_router_logits(c, x, w_gate, lg, s)) != hipSuccess) return hip_fail(e);
+        if ((e = launch_router_logits(c, x, w_gate, lg, part, s)) != hipSuccess)
+            return hip_fail(e);
     }
     StageScope sc(MOE_STAGE_SELECT, s);
     if ((e = launch_fill_i32(expert_counts, c.n_routed, 0, s)) != hipSuccess) return hip_fail(e);

@@ -110,8 +110,9 @@ struct GroupedArgs {
 };
 
 // ---- launchers (each returns hipSuccess or the launch error) ---------------
+int router_splits(const moe_config &c);   // K splits of the router GEMM
 hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
-                                float *logits, hipStream_t s);
+                                float *logits, float *part, hipStream_t s);
 hipError_t launch_select(const moe_config &c, const float *logits, const float *offset,
                          const float *bias, int32_t *idx, float *w, int32_t *counts,
                          double *p_partial, hipStream_t s);

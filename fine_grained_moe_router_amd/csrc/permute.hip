@@ -12,10 +12,12 @@
 
 namespace moe {
 
+// Pairs per chunk: a multiple of 64, at most 256 chunks (small batches get
+// 64-pair chunks, so the placement pass has several blocks and short scans).
 static int perm_chunk(int pairs) {
-    int per = (pairs + 255) / 256;   // at most 256 chunks
-    per = ((per + 255) / 256) * 256;
-    return per < 256 ? 256 : per;
+    int per = (pairs + 255) / 256;
+    per = ((per + 63) / 64) * 64;
+    return per < 64 ? 64 : per;
 }
 
 TileShape tile_shape(const moe_config &c) {
@@ -154,14 +156,32 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
         t2[e] = 0;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < N; e += blockDim.x) {
-        int run = 0;
-        for (int c = 0; c < n_chunks; ++c) {
-            const int v = cc[(size_t)c * N + e];
-            cc[(size_t)c * N + e] = run;
-            run += v;
+    {
+        // Expert e's chunk counts become chunk bases.  Q = 1024 / Np threads
+        // share an expert (Np = N rounded up to a power of two); thread q
+        // takes a contiguous run of chunks and starts from the sum of the
+        // runs before it.
+        int Np = 1;
+        while (Np < N) Np <<= 1;
+        const int Q = 1024 / Np;
+        const int e = threadIdx.x % Np, q = threadIdx.x / Np;
+        const int per = (n_chunks + Q - 1) / Q;
+        const int c0 = min(n_chunks, q * per), c1 = min(n_chunks, c0 + per);
+        int part = 0;
+        if (e < N)
+            for (int c = c0; c < c1; ++c) part += cc[(size_t)c * N + e];
+        tmp[threadIdx.x] = part;
+        __syncthreads();
+        if (e < N) {
+            int run = 0;
+            for (int qq = 0; qq < q; ++qq) run += tmp[qq * Np + e];
+            for (int c = c0; c < c1; ++c) {
+                const int v = cc[(size_t)c * N + e];
+                cc[(size_t)c * N + e] = run;
+                run += v;
+            }
+            if (q == Q - 1) cnt[e] = run;
         }
-        cnt[e] = run;
     }
     if (threadIdx.x == 0 && n_shared > 0) cnt[N] = T;
     __syncthreads();

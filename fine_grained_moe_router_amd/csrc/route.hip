@@ -21,27 +21,33 @@ namespace moe {
 
 using RouterTile = MfmaTile<64, 64, 2, 2, false>;
 
-__global__ __launch_bounds__(RouterTile::NT) void k_router_bf16(int T, int d, int N,
+// Block (m, n, z) computes rows m*64.., logits n*64.. over k-tiles
+// [z*kps, (z+1)*kps) of d.  With one split it writes the logits; with more
+// it writes its partial sum to part[z] and k_router_reduce adds them.
+__global__ __launch_bounds__(RouterTile::NT) void k_router_bf16(int T, int d, int N, int kps,
                                                                 const uint16_t *__restrict__ x,
                                                                 const uint16_t *__restrict__ wg,
-                                                                float *__restrict__ logits) {
+                                                                float *__restrict__ out) {
     __shared__ u32x4 As[2 * RouterTile::LDS_A];
     __shared__ u32x4 Bs[2 * RouterTile::LDS_B];
     const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+    const int k0 = blockIdx.z * kps * kBK;
+    const int K = min(d - k0, kps * kBK);
+    out += (size_t)blockIdx.z * T * N;
     const uint16_t *arow[RouterTile::A_LD];
     const uint16_t *brow[RouterTile::B_LD];
 #pragma unroll
     for (int i = 0; i < RouterTile::A_LD; ++i) {
         int r = m0 + RouterTile::load_row(threadIdx.x, i);
-        arow[i] = (r < T) ? x + (size_t)r * d : nullptr;
+        arow[i] = (r < T) ? x + (size_t)r * d + k0 : nullptr;
     }
 #pragma unroll
     for (int i = 0; i < RouterTile::B_LD; ++i) {
         int r = n0 + RouterTile::load_row(threadIdx.x, i);
-        brow[i] = (r < N) ? wg + (size_t)r * d : nullptr;
+        brow[i] = (r < N) ? wg + (size_t)r * d + k0 : nullptr;
     }
     f32x16 acc[RouterTile::FM][RouterTile::FN];
-    RouterTile::run(arow, brow, d, 0, 1, 0, As, Bs, acc);
+    RouterTile::run(arow, brow, K, 0, 1, 0, As, Bs, acc);
 #pragma unroll
     for (int i = 0; i < RouterTile::FM; ++i)
 #pragma unroll
@@ -50,9 +56,20 @@ __global__ __launch_bounds__(RouterTile::NT) void k_router_bf16(int T, int d, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + RouterTile::out_row(i, r);
-                if (row < T && col < N) logits[(size_t)row * N + col] = acc[i][j][r];
+                if (row < T && col < N) out[(size_t)row * N + col] = acc[i][j][r];
             }
         }
+}
+
+// logits = sum of the split partials, added in split order.
+__global__ __launch_bounds__(256) void k_router_reduce(int n, int splits,
+                                                       const float *__restrict__ part,
+                                                       float *__restrict__ logits) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = part[i];
+    for (int z = 1; z < splits; ++z) v += part[(size_t)z * n + i];
+    logits[i] = v;
 }
 
 __global__ __launch_bounds__(256) void k_router_f32(int T, int d, int N, const float *__restrict__ x,
@@ -74,24 +91,49 @@ __global__ __launch_bounds__(256) void k_router_f32(int T, int d, int N, const f
         }
 }
 
+// K splits of the bf16 router GEMM: enough blocks to cover the CUs when the
+// batch is small (decode), each split at least 8 k-tiles long.
+int router_splits(const moe_config &c) {
+    if (c.dtype != MOE_BF16) return 1;
+    const int tiles = ((c.T + 63) / 64) * ((c.n_routed + 63) / 64);
+    const int nk = c.d_model / kBK;
+    int z = min(min(16, nk / 8), (256 + tiles - 1) / tiles);
+    if (z <= 1) return 1;
+    const int kps = (nk + z - 1) / z;
+    return (nk + kps - 1) / kps;
+}
+
 hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
-                                float *logits, hipStream_t s) {
-    dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64);
-    if (c.dtype == MOE_BF16)
+                                float *logits, float *part, hipStream_t s) {
+    const int z = router_splits(c);
+    if (c.dtype == MOE_BF16) {
+        const int nk = c.d_model / kBK;
+        const int kps = (nk + z - 1) / z;
+        dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64, z);
         hipLaunchKernelGGL(k_router_bf16, grid, dim3(RouterTile::NT), 0, s, c.T, c.d_model,
-                           c.n_routed, (const uint16_t *)x, (const uint16_t *)wg, logits);
-    else
+                           c.n_routed, kps, (const uint16_t *)x, (const uint16_t *)wg,
+                           z > 1 ? part : logits);
+        if (z > 1) {
+            const int n = c.T * c.n_routed;
+            hipLaunchKernelGGL(k_router_reduce, dim3((n + 255) / 256), dim3(256), 0, s, n, z,
+                               part, logits);
+        }
+    } else {
+        dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64);
         hipLaunchKernelGGL(k_router_f32, grid, dim3(256), 0, s, c.T, c.d_model, c.n_routed,
                            (const float *)x, (const float *)wg, logits);
+    }
     return hipGetLastError();
 }
 
 // ============================================================ selection
 
-constexpr int kSelWaves = 4;
+constexpr int kSelWaves = 8;
 constexpr int kMaxTopK = 16;
 
-int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 64 : 16; }
+// One or two tokens per wavefront: the per-token top-K' rounds are a chain of
+// dependent cross-lane steps, so latency is hidden by many resident waves.
+int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 2 * kSelWaves : kSelWaves; }
 
 int select_blocks(const moe_config &c) {
     const int tpb = select_tokens_per_block(c);
@@ -311,24 +353,38 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
 
 // f_i = N' c_i / (K' T); P_i = (1/T) sum over blocks of the partial sums (in
 // block order); loss = alpha1 / N' sum_i f_i P_i (double, fixed tree order).
+// One block.  Expert e's per-block partial sums of s are split over G
+// threads (G = 1024 / Np, Np = N rounded up to a power of two): thread
+// (r, e) adds the partials of blocks r, r + G, ..., and the G sums are then
+// added in r order -- a fixed order, so P is reproducible.
 __global__ __launch_bounds__(1024) void k_balance(int T, int N, int K, const int32_t *__restrict__ c,
                                                   const double *__restrict__ part, int nblk,
                                                   float alpha1, float *__restrict__ f,
                                                   float *__restrict__ P, float *__restrict__ loss) {
     __shared__ double red[1024];
+    int Np = 1;
+    while (Np < N) Np <<= 1;
+    const int G = 1024 / Np;
+    const int e = threadIdx.x % Np, r = threadIdx.x / Np;
+    double s = 0.0;
+    if (part && e < N)
+        for (int b = r; b < nblk; b += G) s += part[(size_t)b * N + e];
+    red[threadIdx.x] = s;
+    __syncthreads();
     double acc = 0.0;
-    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    if (r == 0 && e < N) {
         const double fe = (double)((int64_t)N * c[e]) / (double)((int64_t)K * T);
         f[e] = (float)fe;
         if (part) {
-            double s = 0.0;
-            for (int b = 0; b < nblk; ++b) s += part[(size_t)b * N + e];
-            const double pe = s / (double)T;
+            double tot = 0.0;
+            for (int q = 0; q < G; ++q) tot += red[q * Np + e];
+            const double pe = tot / (double)T;
             if (P) P[e] = (float)pe;
-            acc += fe * pe;
+            acc = fe * pe;
         }
     }
     if (!loss) return;
+    __syncthreads();
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int o = blockDim.x / 2; o > 0; o >>= 1) {
@@ -340,7 +396,6 @@ __global__ __launch_bounds__(1024) void k_balance(int T, int N, int K, const int
         loss[1] = (float)red[0];
     }
 }
-
 hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts,
                                 const double *p_partial, int n_blocks, float alpha1, float *f,
                                 float *P, float *loss, hipStream_t s) {

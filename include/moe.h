@@ -125,7 +125,10 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which);
  *              MOE_LOGITS_OUT, else NULL.  Always the raw x W_g^T (no offset).
  *   topk_idx   [T][K'] int32 out;  topk_w [T][K'] fp32 out
  *   expert_counts [N'] int32 out
- *   workspace  >= moe_workspace_bytes(cfg, MOE_WS_ROUTE) bytes
+ *   workspace  >= moe_workspace_bytes(cfg, MOE_WS_ROUTE) bytes; required
+ *              whenever the router GEMM runs (not with MOE_LOGITS_IN or
+ *              HASH): it holds the logits (unless MOE_LOGITS_OUT) and, for
+ *              small batches, the partial sums of a K-split GEMM
  * Errors: INVALID_ARG for a NULL required pointer, an out-of-range field,
  * HASH with K' != 1, missing token_ids, or p_partial under HASH;
  * UNSUPPORTED for d or widths not multiples of 64; WORKSPACE when ws_bytes

@@ -99,6 +99,17 @@ def route(L, c, x=P, wg=P, off=None, bias=None, tid=None, logits=None, idx=P, w=
                        ws_bytes, None)
 
 
+def test_route_workspace_holds_split_partials():
+    # A small batch splits the router GEMM along d: the route workspace then
+    # holds the logits plus one [T][N'] partial per split; a large batch does not split.
+    small, large = B.make_config(CONFIGS["v3_decode"]), B.make_config(CONFIGS["v3_prefill"])
+    tn_small = CONFIGS["v3_decode"].T * CONFIGS["v3_decode"].n_routed * 4
+    tn_large = CONFIGS["v3_prefill"].T * CONFIGS["v3_prefill"].n_routed * 4
+    assert B.workspace_bytes(small, B.WS_ROUTE) >= 3 * tn_small
+    assert B.workspace_bytes(small, B.WS_ROUTE) % tn_small == 0
+    assert B.workspace_bytes(large, B.WS_ROUTE) == tn_large
+
+
 def test_route_argument_errors(L):
     c = cfg_of("v3_decode")
     assert route(L, c, idx=None) == B.MOE_ERR_INVALID_ARG
@@ -115,6 +126,7 @@ def test_route_argument_errors(L):
     cout = cfg_of("v3_decode")
     cout.flags = B.LOGITS_OUT
     assert route(L, cout, logits=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, cout, logits=P, ws=None) == B.MOE_ERR_INVALID_ARG  # split partials need it
     h = cfg_of("v4_hash")
     assert route(L, h, tid=None) == B.MOE_ERR_INVALID_ARG       # hash needs token ids
     assert route(L, h, tid=P, pstat=P) == B.MOE_ERR_INVALID_ARG  # no P under hash

@@ -153,12 +153,20 @@ static void token_scores(int scoring, int64_t n, const float *l, double *s64,
  * Returns 0, or -1 on an invalid argument. */
 int oracle_route(int64_t n_tok, int64_t n_routed, int64_t top_k, int scoring,
                  int renorm, const float *logits, const float *offset,
-                 const float *bias, const uint32_t *token_ids, int32_t *idx,
+                 const float *bias, const uint32_t *token_ids,
+                 int64_t n_groups, int64_t topk_groups, int32_t *idx,
                  float *gate, float *s32_out, double *gap_out)
 {
     if (n_tok < 0 || n_routed < 1 || top_k < 1 || top_k > n_routed)
         return -1;
+    if (n_groups < 0 || (n_groups > 0 && (n_routed % n_groups != 0 ||
+                                          topk_groups < 1 ||
+                                          topk_groups > n_groups ||
+                                          topk_groups * (n_routed / n_groups) < top_k)))
+        return -1;
     if (scoring == OR_HASH) {
+        if (n_groups > 0)
+            return -1;
         if (!token_ids || top_k != 1)
             return -1;
         for (int64_t t = 0; t < n_tok; ++t) {
@@ -180,7 +188,12 @@ int oracle_route(int64_t n_tok, int64_t n_routed, int64_t top_k, int scoring,
         float *s32 = malloc(sizeof(float) * n_routed);
         float *key = malloc(sizeof(float) * n_routed);
         char *taken = malloc((size_t)n_routed);
-        if (!l || !s64 || !s32 || !key || !taken) {
+        char *allowed = malloc((size_t)n_routed);
+        int64_t ng = n_groups > 0 ? n_groups : 1;
+        float *gkey = malloc(sizeof(float) * ng);
+        double *gscore = malloc(sizeof(double) * ng);
+        char *gtaken = malloc((size_t)ng);
+        if (!l || !s64 || !s32 || !key || !taken || !allowed || !gkey || !gscore || !gtaken) {
 #pragma omp atomic write
             bad = 1;
         } else {
@@ -194,12 +207,45 @@ int oracle_route(int64_t n_tok, int64_t n_routed, int64_t top_k, int scoring,
                 for (int64_t i = 0; i < n_routed; ++i) {
                     key[i] = bias ? s32[i] + bias[i] : l[i]; /* fp32 add */
                     taken[i] = 0;
+                    allowed[i] = 1;
+                }
+                /* node-limited routing ([P3] sec. 4): only experts of the
+                 * topk_groups groups with the largest best key may be taken */
+                double group_gap = INFINITY;
+                if (n_groups > 0) {
+                    const int64_t gsz = n_routed / n_groups;
+                    for (int64_t g = 0; g < n_groups; ++g) {
+                        gkey[g] = key[g * gsz];
+                        gscore[g] = s64[g * gsz] + (bias ? (double)bias[g * gsz] : 0.0);
+                        for (int64_t i = g * gsz + 1; i < (g + 1) * gsz; ++i) {
+                            if (key[i] > gkey[g])
+                                gkey[g] = key[i];
+                            double v = s64[i] + (bias ? (double)bias[i] : 0.0);
+                            if (v > gscore[g])
+                                gscore[g] = v;
+                        }
+                        gtaken[g] = 0;
+                    }
+                    double last = 0.0;
+                    for (int64_t m = 0; m < topk_groups; ++m) {
+                        int64_t best = -1;
+                        for (int64_t g = 0; g < n_groups; ++g)
+                            if (!gtaken[g] && (best < 0 || gkey[g] > gkey[best]))
+                                best = g;
+                        gtaken[best] = 1;
+                        last = gscore[best];
+                    }
+                    for (int64_t g = 0; g < n_groups; ++g)
+                        if (!gtaken[g] && last - gscore[g] < group_gap)
+                            group_gap = last - gscore[g];
+                    for (int64_t i = 0; i < n_routed; ++i)
+                        allowed[i] = gtaken[i / gsz];
                 }
                 /* top-k by (key desc, index asc): k passes of a plain argmax */
                 for (int64_t k = 0; k < top_k; ++k) {
                     int64_t best = -1;
                     for (int64_t i = 0; i < n_routed; ++i) {
-                        if (taken[i])
+                        if (taken[i] || !allowed[i])
                             continue;
                         if (best < 0 || key[i] > key[best])
                             best = i;
@@ -216,18 +262,19 @@ int oracle_route(int64_t n_tok, int64_t n_routed, int64_t top_k, int scoring,
                     gate[t * top_k + k] = renorm ? (float)(s / den) : (float)s;
                 }
                 if (gap_out) {
-                    if (top_k == n_routed) {
-                        gap_out[t] = INFINITY;
-                    } else {
-                        int64_t nxt = -1;
-                        for (int64_t i = 0; i < n_routed; ++i)
-                            if (!taken[i] && (nxt < 0 || key[i] > key[nxt]))
-                                nxt = i;
+                    /* next candidate: the best allowed expert not taken */
+                    int64_t nxt = -1;
+                    for (int64_t i = 0; i < n_routed; ++i)
+                        if (!taken[i] && allowed[i] && (nxt < 0 || key[i] > key[nxt]))
+                            nxt = i;
+                    double g = INFINITY;
+                    if (nxt >= 0) {
                         int64_t kth = idx[t * top_k + top_k - 1];
                         double a = s64[kth] + (bias ? (double)bias[kth] : 0.0);
                         double b = s64[nxt] + (bias ? (double)bias[nxt] : 0.0);
-                        gap_out[t] = a - b;
+                        g = a - b;
                     }
+                    gap_out[t] = g < group_gap ? g : group_gap;
                 }
                 if (s32_out)
                     memcpy(s32_out + t * n_routed, s32, sizeof(float) * n_routed);
@@ -238,6 +285,10 @@ int oracle_route(int64_t n_tok, int64_t n_routed, int64_t top_k, int scoring,
         free(s32);
         free(key);
         free(taken);
+        free(allowed);
+        free(gkey);
+        free(gscore);
+        free(gtaken);
     }
     return bad ? -1 : 0;
 }
@@ -277,6 +328,81 @@ void oracle_balance_stats(int64_t n_tok, int64_t n_routed, int64_t top_k,
     if (loss2) {
         loss2[0] = alpha1 / (double)n_routed * raw;
         loss2[1] = raw;
+    }
+}
+
+/* [P3] sec. 3, change 2: the in-sequence balance loss
+ * L_seq = beta * sum_i f_i^seq p_i^seq, per segment (sequence) s of the
+ * batch: tokens seg_off[s] .. seg_off[s+1]-1.  Readings: f_i^seq is
+ * normalised like f_i of [P1] (N'/(K' T_s) times the selections of i in the
+ * segment), p_i^seq is the mean raw score s32 of i over the segment's tokens
+ * (as P_i), and an empty segment gives f = p = 0 and L = 0.
+ * Outputs f_seq, p_seq [n_seg][n_routed], loss [n_seg], all double. */
+void oracle_seq_balance_stats(int64_t n_tok, int64_t n_routed, int64_t top_k,
+                              int64_t n_seg, const int64_t *seg_off,
+                              const int32_t *idx, const float *scores, double beta,
+                              double *f_seq, double *p_seq, double *loss)
+{
+    for (int64_t s = 0; s < n_seg; ++s) {
+        const int64_t t0 = seg_off[s], t1 = seg_off[s + 1], ts = t1 - t0;
+        double raw = 0.0;
+        for (int64_t i = 0; i < n_routed; ++i) {
+            int64_t c = 0;
+            double acc = 0.0;
+            for (int64_t t = t0; t < t1; ++t) {
+                for (int64_t k = 0; k < top_k; ++k)
+                    if (idx[t * top_k + k] == i)
+                        c += 1;
+                acc += (double)scores[t * n_routed + i];
+            }
+            double f = ts > 0 ? (double)(n_routed * c) / (double)(top_k * ts) : 0.0;
+            double p = ts > 0 ? acc / (double)ts : 0.0;
+            f_seq[s * n_routed + i] = f;
+            p_seq[s * n_routed + i] = p;
+            raw += f * p;
+        }
+        loss[s] = beta * raw;
+    }
+    (void)n_tok;
+}
+
+/* [P1] device-level balance loss: the routed experts split into n_dev
+ * groups E_d; f'_d = mean of f_j over E_d, P'_d = sum of P_j over E_d,
+ * L_DevBal = alpha2 * sum_d f'_d P'_d.  Reading: the groups are n_dev
+ * contiguous runs of N'/n_dev experts.  f and P are the fp32 outputs of the
+ * expert-level statistics. */
+void oracle_device_balance_stats(int64_t n_routed, int64_t n_dev, const float *f,
+                                 const float *P, double alpha2, double *f_dev,
+                                 double *P_dev, double *loss)
+{
+    const int64_t gsz = n_routed / n_dev;
+    double raw = 0.0;
+    for (int64_t d = 0; d < n_dev; ++d) {
+        double fs = 0.0, ps = 0.0;
+        for (int64_t j = d * gsz; j < (d + 1) * gsz; ++j) {
+            fs += (double)f[j];
+            ps += (double)P[j];
+        }
+        f_dev[d] = fs / (double)gsz;
+        P_dev[d] = ps;
+        raw += f_dev[d] * P_dev[d];
+    }
+    *loss = alpha2 * raw;
+}
+
+/* [P3] sec. 3, the aux-loss-free bias update of V3:
+ * b_i <- b_i + alpha (f* - f_i), f* = K'/N' the uniform share and f_i the
+ * share of tokens routed to expert i over the window (counts c_i over
+ * n_tok tokens: f_i = c_i / n_tok, so sum_i f_i = K' = sum_i f*).
+ * Evaluated in double, rounded once to fp32. */
+void oracle_bias_update(int64_t n_routed, int64_t top_k, int64_t n_tok,
+                        const int32_t *counts, double alpha, const float *bias_in,
+                        float *bias_out)
+{
+    const double target = (double)top_k / (double)n_routed;
+    for (int64_t i = 0; i < n_routed; ++i) {
+        double share = (double)counts[i] / (double)n_tok;
+        bias_out[i] = (float)((double)bias_in[i] + alpha * (target - share));
     }
 }
 

@@ -67,12 +67,19 @@ def _load():
     lib.oracle_threads.restype = i32
     lib.oracle_fmix32.argtypes = [ctypes.c_uint32]
     lib.oracle_fmix32.restype = ctypes.c_uint32
-    lib.oracle_route.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_route.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, i64, i64,
+                                 vp, vp, vp, vp]
     lib.oracle_route.restype = i32
     lib.oracle_counts.argtypes = [i64, i64, i64, vp, vp]
     lib.oracle_counts.restype = None
     lib.oracle_balance_stats.argtypes = [i64, i64, i64, vp, vp, dbl, vp, vp, vp]
     lib.oracle_balance_stats.restype = None
+    lib.oracle_seq_balance_stats.argtypes = [i64, i64, i64, i64, vp, vp, vp, dbl, vp, vp, vp]
+    lib.oracle_seq_balance_stats.restype = None
+    lib.oracle_device_balance_stats.argtypes = [i64, i64, vp, vp, dbl, vp, vp, vp]
+    lib.oracle_device_balance_stats.restype = None
+    lib.oracle_bias_update.argtypes = [i64, i64, i64, vp, dbl, vp, vp]
+    lib.oracle_bias_update.restype = None
     lib.oracle_forward.argtypes = [i64, vp, i64, i64, i64, i64, i64, i64, i32,
                                    vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_forward.restype = None
@@ -126,14 +133,20 @@ def router_logits(x: np.ndarray, w_gate: np.ndarray, tokens=None) -> np.ndarray:
 
 
 def route(logits, n_routed: int, top_k: int, scoring: str, renorm: bool,
-          offset=None, bias=None, token_ids=None):
+          offset=None, bias=None, token_ids=None, n_groups: int = 0, topk_groups: int = 0):
     """Scores, selection and gates for every row.
 
     Follows the top-k gate equation of the DeepSeekMoE notes ("core design 1"),
     the V4 book ch. 02 sec. 1 (sigmoid, renormalisation), sec. 2 (sqrt of
     softplus), sec. 3 (selection score s + b) and sec. 5 (hash routing).
+    With n_groups > 0, node-limited routing (V4 book ch. 02 sec. 4, V3's
+    limit of M nodes per token): the experts form n_groups contiguous equal
+    groups, the topk_groups groups with the largest best selection key are
+    kept (ties: lower group index), and top-K' runs over their experts.
     Returns (idx int32 [n][K'], gate fp32 [n][K'], s32 fp32 [n][N'] or None,
-    gap fp64 [n]).
+    gap fp64 [n]); with groups the gap is the smaller of the expert gap
+    within the kept groups and the gap between the last kept and the best
+    dropped group (best score of a group in score units).
     """
     code = SCORING[scoring]
     if code == SCORING["hash"]:
@@ -151,6 +164,7 @@ def route(logits, n_routed: int, top_k: int, scoring: str, renorm: bool,
     rc = _load().oracle_route(n, n_routed, top_k, code, int(bool(renorm)), _ptr(lg),
                               _ptr(_c(offset, np.float32)), _ptr(_c(bias, np.float32)),
                               _ptr(token_ids if code == SCORING["hash"] else None),
+                              int(n_groups), int(topk_groups),
                               _ptr(idx), _ptr(gate), _ptr(s32), _ptr(gap))
     if rc != 0:
         raise ValueError("oracle_route rejected its arguments")
@@ -182,6 +196,51 @@ def balance_stats(cnt: np.ndarray, s32, n_tok: int, top_k: int, alpha1: float):
     if s is None:
         return f, None, None
     return f, P, loss
+
+
+def seq_balance_stats(idx, s32, seg_off, beta: float):
+    """In-sequence balance statistics (V4 book ch. 02 sec. 3, change 2):
+    per segment s (tokens seg_off[s] .. seg_off[s+1]-1) f_i^seq (normalised
+    like the notes' f_i), p_i^seq (mean raw score) and
+    L_seq = beta * sum_i f_i^seq p_i^seq.  Empty segments give zeros.
+    Returns (f_seq [S][N'], p_seq [S][N'], loss [S]), all fp64."""
+    idx, s32 = _c(idx, np.int32), _c(s32, np.float32)
+    off = _c(np.asarray(seg_off), np.int64)
+    T, K = idx.shape
+    N = s32.shape[1]
+    S = len(off) - 1
+    assert s32.shape == (T, N) and off[0] >= 0 and off[-1] <= T and np.all(np.diff(off) >= 0)
+    f = np.empty((S, N), np.float64)
+    p = np.empty((S, N), np.float64)
+    loss = np.empty(S, np.float64)
+    _load().oracle_seq_balance_stats(T, N, K, S, _ptr(off), _ptr(idx), _ptr(s32), float(beta),
+                                     _ptr(f), _ptr(p), _ptr(loss))
+    return f, p, loss
+
+
+def device_balance_stats(f, P, n_dev: int, alpha2: float):
+    """Device-level balance loss of the DeepSeekMoE notes over n_dev contiguous
+    groups of experts: f'_d (mean f), P'_d (sum P), L_DevBal.  f, P are the
+    fp32 expert-level statistics.  Returns (f_dev, P_dev, loss) in fp64."""
+    f, P = _c(f, np.float32), _c(P, np.float32)
+    N = len(f)
+    assert len(P) == N and n_dev >= 1 and N % n_dev == 0
+    fd = np.empty(n_dev, np.float64)
+    pd = np.empty(n_dev, np.float64)
+    loss = np.empty(1, np.float64)
+    _load().oracle_device_balance_stats(N, n_dev, _ptr(f), _ptr(P), float(alpha2), _ptr(fd),
+                                        _ptr(pd), _ptr(loss))
+    return fd, pd, float(loss[0])
+
+
+def bias_update(cnt, n_tok: int, top_k: int, alpha: float, bias) -> np.ndarray:
+    """Aux-loss-free bias update (V4 book ch. 02 sec. 3, V3):
+    b_i + alpha (K'/N' - c_i / n_tok), in double, rounded to fp32."""
+    cnt, b = _c(cnt, np.int32), _c(bias, np.float32)
+    N = len(cnt)
+    out = np.empty(N, np.float32)
+    _load().oracle_bias_update(N, top_k, n_tok, _ptr(cnt), float(alpha), _ptr(b), _ptr(out))
+    return out
 
 
 def forward(x, idx, gate, w13, w2, w13s, w2s, tokens=None) -> np.ndarray:

@@ -21,10 +21,11 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 SCORING = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "hash": 3}
 DTYPE = {"f32": 0, "bf16": 1}
 LOGITS_IN, LOGITS_OUT = 1, 2
-WS_ROUTE, WS_FORWARD, WS_PSTAT = 0, 1, 2
+WS_ROUTE, WS_FORWARD, WS_PSTAT, WS_SEQSTAT = 0, 1, 2, 3
 STAGES = ("router_gemm", "select", "permute", "gate_up", "down", "combine", "stats")
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_balance_stats",
+           "moe_seq_balance_stats", "moe_device_balance_stats", "moe_bias_update",
            "moe_status_string", "moe_profile_enable", "moe_profile_collect")
 
 
@@ -40,7 +41,8 @@ class MoeConfig(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("scoring", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32)]
 
 
 class StageTimes(ctypes.Structure):
@@ -68,6 +70,12 @@ def lib():
     L.moe_forward.restype = i32
     L.moe_balance_stats.argtypes = [cfgp, vp, vp, f32, vp, vp, vp, vp]
     L.moe_balance_stats.restype = i32
+    L.moe_seq_balance_stats.argtypes = [cfgp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.moe_seq_balance_stats.restype = i32
+    L.moe_device_balance_stats.argtypes = [cfgp, vp, vp, i32, f32, vp, vp, vp, vp]
+    L.moe_device_balance_stats.restype = i32
+    L.moe_bias_update.argtypes = [cfgp, vp, ctypes.c_int64, f32, vp, vp]
+    L.moe_bias_update.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_profile_enable.argtypes = [i32]
@@ -85,7 +93,7 @@ def status_string(status: int) -> str:
 def make_config(cfg: LayerConfig, flags: int = 0, T: Optional[int] = None) -> MoeConfig:
     return MoeConfig(cfg.T if T is None else T, cfg.d_model, cfg.n_routed, cfg.top_k,
                      cfg.n_shared, cfg.d_ff, cfg.d_ff_shared, SCORING[cfg.scoring],
-                     int(cfg.renorm), DTYPE[cfg.dtype], flags)
+                     int(cfg.renorm), DTYPE[cfg.dtype], flags, cfg.n_groups, cfg.topk_groups)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -210,6 +218,62 @@ def balance_stats(cfg: LayerConfig, counts, pstat, alpha1: Optional[float] = Non
                                  _p(f), _p(P), _p(loss), _stream(stream))
     _check(rc, "moe_balance_stats")
     return f, P, loss
+
+
+def seq_balance_stats(cfg: LayerConfig, logits, idx, seg_offsets, beta: float, offset=None,
+                      out=None, workspace=None, stream=None):
+    """moe_seq_balance_stats.  seg_offsets: int32 [S+1] on the GPU.
+    Returns (f_seq [S][N'], p_seq [S][N'], loss [S])."""
+    c = make_config(cfg)
+    T, N, K = cfg.T, cfg.n_routed, cfg.top_k
+    _need(logits, (T, N), torch.float32, "logits")
+    _need(idx, (T, K), torch.int32, "idx")
+    S = seg_offsets.numel() - 1
+    _need(seg_offsets, (S + 1,), torch.int32, "seg_offsets")
+    if offset is not None:
+        _need(offset, (N,), torch.float32, "offset")
+    dev = logits.device
+    o = out or {}
+    f = o.get("f_seq") if o.get("f_seq") is not None else torch.empty((S, N), dtype=torch.float32, device=dev)
+    p = o.get("p_seq") if o.get("p_seq") is not None else torch.empty((S, N), dtype=torch.float32, device=dev)
+    loss = o.get("loss") if o.get("loss") is not None else torch.empty(S, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(c, WS_SEQSTAT, dev)
+    rc = lib().moe_seq_balance_stats(ctypes.byref(c), _p(logits), _p(offset), _p(idx),
+                                     _p(seg_offsets), S, ctypes.c_float(beta), _p(f), _p(p),
+                                     _p(loss), _p(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "moe_seq_balance_stats")
+    return f, p, loss
+
+
+def device_balance_stats(cfg: LayerConfig, f, P, n_dev: int, alpha2: float, want_loss=True,
+                         stream=None):
+    """moe_device_balance_stats.  Returns (f_dev [n_dev], P_dev [n_dev], loss [1] or None)."""
+    c = make_config(cfg)
+    N = cfg.n_routed
+    _need(f, (N,), torch.float32, "f")
+    _need(P, (N,), torch.float32, "P")
+    dev = f.device
+    fd = torch.empty(n_dev, dtype=torch.float32, device=dev)
+    pd = torch.empty(n_dev, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if want_loss else None
+    rc = lib().moe_device_balance_stats(ctypes.byref(c), _p(f), _p(P), n_dev,
+                                        ctypes.c_float(alpha2), _p(fd), _p(pd), _p(loss),
+                                        _stream(stream))
+    _check(rc, "moe_device_balance_stats")
+    return fd, pd, loss
+
+
+def bias_update(cfg: LayerConfig, counts, n_tokens: int, alpha: float, bias, stream=None):
+    """moe_bias_update: updates `bias` ([N'] fp32 on the GPU) in place and returns it."""
+    c = make_config(cfg)
+    N = cfg.n_routed
+    _need(counts, (N,), torch.int32, "counts")
+    _need(bias, (N,), torch.float32, "bias")
+    rc = lib().moe_bias_update(ctypes.byref(c), _p(counts), int(n_tokens), ctypes.c_float(alpha),
+                               _p(bias), _stream(stream))
+    _check(rc, "moe_bias_update")
+    return bias
 
 
 def profile_enable(max_records: int):

@@ -35,6 +35,8 @@ class LayerConfig:
     seed: int = 0
     family: str = ""       # configs sharing a family share their weights
     m: int = 1             # segmentation factor (documentation only)
+    n_groups: int = 0      # node-limited routing: expert groups (0: no limit)
+    topk_groups: int = 0   # M: groups one token may draw its experts from
 
     @property
     def weight_family(self) -> str:

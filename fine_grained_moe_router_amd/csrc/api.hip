@@ -52,6 +52,15 @@ int validate(const moe_config *c) {
     if (c->flags & ~(MOE_LOGITS_IN | MOE_LOGITS_OUT)) return MOE_ERR_INVALID_ARG;
     if ((c->flags & MOE_LOGITS_IN) && (c->flags & MOE_LOGITS_OUT)) return MOE_ERR_INVALID_ARG;
     if (c->scoring == MOE_ROUTE_HASH && (c->top_k != 1 || c->flags)) return MOE_ERR_INVALID_ARG;
+    if (c->n_groups < 0 || c->n_groups > 64) return MOE_ERR_INVALID_ARG;
+    if (c->n_groups > 0) {
+        if (c->scoring == MOE_ROUTE_HASH || c->n_routed % c->n_groups) return MOE_ERR_INVALID_ARG;
+        if (c->topk_groups < 1 || c->topk_groups > c->n_groups) return MOE_ERR_INVALID_ARG;
+        if ((long long)c->topk_groups * (c->n_routed / c->n_groups) < c->top_k)
+            return MOE_ERR_INVALID_ARG;
+    } else if (c->topk_groups != 0) {
+        return MOE_ERR_INVALID_ARG;
+    }
     if (c->d_model % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
     if (c->n_shared > 0 && c->d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
     const long long P = (long long)c->T * c->top_k;
@@ -90,6 +99,7 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which) {
         case MOE_WS_ROUTE: return route_ws(*cfg);
         case MOE_WS_FORWARD: return fwd_layout(*cfg).total;
         case MOE_WS_PSTAT: return pstat_bytes(*cfg);
+        case MOE_WS_SEQSTAT: return cfg->scoring == MOE_ROUTE_HASH ? 0 : route_logits_bytes(*cfg);
         default: return 0;
     }
 }
@@ -216,6 +226,46 @@ int moe_balance_stats(const moe_config *cfg, const int32_t *expert_counts, const
     StageScope sc(MOE_STAGE_STATS, s);
     hipError_t e = launch_balance_stats(c, expert_counts, (P || loss) ? (const double *)p_partial : nullptr,
                                         select_blocks(c), alpha1, f, P, loss, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_seq_balance_stats(const moe_config *cfg, const float *logits, const float *logit_offset,
+                          const int32_t *topk_idx, const int32_t *seg_offsets, int32_t n_seg,
+                          float beta, float *f_seq, float *p_seq, float *loss_seq,
+                          void *workspace, size_t ws_bytes, void *stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    const moe_config &c = *cfg;
+    if (c.scoring == MOE_ROUTE_HASH || n_seg < 1) return MOE_ERR_INVALID_ARG;
+    if (!logits || !topk_idx || !seg_offsets || !f_seq || !p_seq || !loss_seq || !workspace)
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < route_logits_bytes(c)) return MOE_ERR_WORKSPACE;
+    hipError_t e = launch_seq_stats(c, logits, logit_offset, topk_idx, seg_offsets, n_seg, beta,
+                                    (float *)workspace, f_seq, p_seq, loss_seq,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_device_balance_stats(const moe_config *cfg, const float *f, const float *P, int32_t n_dev,
+                             float alpha2, float *f_dev, float *P_dev, float *loss,
+                             void *stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    const moe_config &c = *cfg;
+    if (!f || !P || !f_dev || !P_dev) return MOE_ERR_INVALID_ARG;
+    if (n_dev < 1 || c.n_routed % n_dev) return MOE_ERR_INVALID_ARG;
+    hipError_t e = launch_device_stats(c, f, P, n_dev, alpha2, f_dev, P_dev, loss,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_bias_update(const moe_config *cfg, const int32_t *expert_counts, int64_t n_tokens,
+                    float alpha, float *bias, void *stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!expert_counts || !bias || n_tokens < 1) return MOE_ERR_INVALID_ARG;
+    hipError_t e = launch_bias_update(*cfg, expert_counts, n_tokens, alpha, bias,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

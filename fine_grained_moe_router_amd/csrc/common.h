@@ -113,6 +113,15 @@ struct GroupedArgs {
 int router_splits(const moe_config &c);   // K splits of the router GEMM
 hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
                                 float *logits, float *part, hipStream_t s);
+hipError_t launch_seq_stats(const moe_config &c, const float *logits, const float *offset,
+                            const int32_t *idx, const int32_t *seg_off, int n_seg, float beta,
+                            float *scores, float *f_seq, float *p_seq, float *loss,
+                            hipStream_t s);
+hipError_t launch_device_stats(const moe_config &c, const float *f, const float *P, int n_dev,
+                               float alpha2, float *f_dev, float *P_dev, float *loss,
+                               hipStream_t s);
+hipError_t launch_bias_update(const moe_config &c, const int32_t *counts, long long n_tok,
+                              float alpha, float *bias, hipStream_t s);
 hipError_t launch_select(const moe_config &c, const float *logits, const float *offset,
                          const float *bias, int32_t *idx, float *w, int32_t *counts,
                          double *p_partial, hipStream_t s);

@@ -149,14 +149,71 @@ __device__ __forceinline__ double score_pointwise(int scoring, float l) {
     return sqrt(sp);
 }
 
+// Logits (plus the optional offset, an fp32 add) and scores s32 of one token
+// held by one wavefront: lane `lane` owns experts lane + 64 j, j < J.
+// Scores are evaluated in double from the fp32 logit and rounded once.
+template <int J>
+__device__ __forceinline__ void wave_token_scores(int N, int scoring, const float *row,
+                                                  const float *offset, int lane, float (&l)[J],
+                                                  float (&s32)[J]) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = lane + 64 * j;
+        float v = (e < N) ? row[e] : -INFINITY;
+        if (offset && e < N) v = v + offset[e];  // fp32 add
+        l[j] = v;
+    }
+    if (scoring == MOE_SCORE_SOFTMAX) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < J; ++j) m = fmaxf(m, l[j]);
+        m = wave_max_f32(m);
+        double ex[J], part = 0.0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + 64 * j;
+            ex[j] = (e < N) ? exp((double)l[j] - (double)m) : 0.0;
+            part += ex[j];
+        }
+        const double sum = wave_sum_f64(part);
+#pragma unroll
+        for (int j = 0; j < J; ++j) s32[j] = (float)(ex[j] / sum);
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + 64 * j;
+            s32[j] = (e < N) ? (float)score_pointwise(scoring, l[j]) : 0.0f;
+        }
+    }
+}
+
+// Wave-wide argmax of (v desc, index asc) over the lanes whose idx is not
+// 0x7fffffff; every lane receives the winner.
+__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(v, o, kWave);
+        const int oi = __shfl_xor(idx, o, kWave);
+        if (oi != 0x7fffffff && (idx == 0x7fffffff || ov > v || (ov == v && oi < idx))) {
+            v = ov;
+            idx = oi;
+        }
+    }
+}
+
 // One wavefront per token.  Lane `lane` owns experts lane + 64 j, j < J.
+// Node-limited routing (n_groups > 0): the experts of the topk_groups groups
+// with the largest best key are the only candidates; the others are marked
+// taken before the top-K' rounds.
 template <int J>
 __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
-    int T, int N, int K, int scoring, int renorm, int tpb, const float *__restrict__ logits,
-    const float *__restrict__ offset, const float *__restrict__ bias, int32_t *__restrict__ idx_out,
-    float *__restrict__ w_out, int32_t *__restrict__ counts, double *__restrict__ p_partial) {
+    int T, int N, int K, int scoring, int renorm, int tpb, int n_groups, int topk_groups,
+    const float *__restrict__ logits, const float *__restrict__ offset,
+    const float *__restrict__ bias, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+    int32_t *__restrict__ counts, double *__restrict__ p_partial) {
     __shared__ int32_t hist[J * kWave];
     __shared__ double psum[kSelWaves][J * kWave];
+    __shared__ float kbuf[kSelWaves][J * kWave];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     for (int e = threadIdx.x; e < J * kWave; e += blockDim.x) hist[e] = 0;
@@ -170,45 +227,45 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
     const int t1 = min(T, t0 + tpb);
     for (int t = t0 + wave; t < t1; t += kSelWaves) {
         float l[J], key[J], s32[J];
-        const float *row = logits + (size_t)t * N;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int e = lane + 64 * j;
-            float v = (e < N) ? row[e] : -INFINITY;
-            if (offset && e < N) v = v + offset[e];  // fp32 add
-            l[j] = v;
-        }
-        // ---- scores: double from the fp32 logit, rounded once to fp32
-        if (scoring == MOE_SCORE_SOFTMAX) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < J; ++j) m = fmaxf(m, l[j]);
-            m = wave_max_f32(m);
-            double ex[J], part = 0.0;
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int e = lane + 64 * j;
-                ex[j] = (e < N) ? exp((double)l[j] - (double)m) : 0.0;
-                part += ex[j];
-            }
-            const double sum = wave_sum_f64(part);
-#pragma unroll
-            for (int j = 0; j < J; ++j) s32[j] = (float)(ex[j] / sum);
-        } else {
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int e = lane + 64 * j;
-                s32[j] = (e < N) ? (float)score_pointwise(scoring, l[j]) : 0.0f;
-            }
-        }
+        wave_token_scores<J>(N, scoring, logits + (size_t)t * N, offset, lane, l, s32);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int e = lane + 64 * j;
             key[j] = bias ? ((e < N) ? s32[j] + bias[e] : -INFINITY) : l[j];  // fp32 add
             if (e < N) pacc[j] += (double)s32[j];
         }
-        // ---- top-K': K' rounds of a wave-wide argmax on (key desc, index asc)
         uint32_t taken = 0;
+        if (n_groups > 0) {
+            // best key of each group (lane g holds group g), via this wave's LDS row
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (lane + 64 * j < N) kbuf[wave][lane + 64 * j] = key[j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int gsz = N / n_groups;
+            float gk = -INFINITY;
+            if (lane < n_groups) {
+                gk = kbuf[wave][lane * gsz];
+                for (int i = 1; i < gsz; ++i) gk = fmaxf(gk, kbuf[wave][lane * gsz + i]);
+            }
+            __builtin_amdgcn_wave_barrier();   // reads done before the next token's writes
+            uint64_t chosen = 0;
+            bool gdone = false;
+            for (int m = 0; m < topk_groups; ++m) {
+                float v = gk;
+                int gi = (lane < n_groups && !gdone) ? lane : 0x7fffffff;
+                wave_argmax(v, gi);
+                chosen |= 1ull << gi;
+                if (lane == gi) gdone = true;
+            }
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int e = lane + 64 * j;
+                if (e < N && !((chosen >> (e / gsz)) & 1ull)) taken |= 1u << j;
+            }
+        }
+        // ---- top-K': K' rounds of a wave-wide argmax on (key desc, index asc)
         int sel[kMaxTopK];
         float sv[kMaxTopK];
 #pragma unroll
@@ -226,16 +283,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
                         bi = e;
                     }
                 }
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    const float ok = __shfl_xor(bk, o, kWave);
-                    const int oi = __shfl_xor(bi, o, kWave);
-                    if (oi != 0x7fffffff &&
-                        (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi))) {
-                        bk = ok;
-                        bi = oi;
-                    }
-                }
+                wave_argmax(bk, bi);
                 float mine = 0.0f;
 #pragma unroll
                 for (int j = 0; j < J; ++j)
@@ -286,7 +334,8 @@ hipError_t launch_select(const moe_config &c, const float *logits, const float *
     dim3 grid(select_blocks(c)), block(kSelWaves * kWave);
 #define MOE_SEL(JJ)                                                                            \
     hipLaunchKernelGGL(k_select<JJ>, grid, block, 0, s, c.T, c.n_routed, c.top_k, c.scoring,   \
-                       c.renorm, tpb, logits, offset, bias, idx, w, counts, p_partial)
+                       c.renorm, tpb, c.n_groups, c.topk_groups, logits, offset, bias, idx, w, \
+                       counts, p_partial)
     if (J <= 1) MOE_SEL(1);
     else if (J <= 2) MOE_SEL(2);
     else if (J <= 4) MOE_SEL(4);
@@ -307,6 +356,172 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
     h *= 0xc2b2ae35u;
     h ^= h >> 16;
     return h;
+}
+
+// ============================================================ segment and device statistics
+
+// Score rows: one wavefront per token writes s32[t][0..N) exactly as k_select
+// computes them (V4 book ch. 02 sec. 3, change 2 needs the raw scores).
+template <int J>
+__global__ __launch_bounds__(kSelWaves * kWave) void k_scores(int T, int N, int scoring,
+                                                              const float *__restrict__ logits,
+                                                              const float *__restrict__ offset,
+                                                              float *__restrict__ s32_out) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float l[J], s32[J];
+    wave_token_scores<J>(N, scoring, logits + (size_t)t * N, offset, lane, l, s32);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        if (lane + 64 * j < N) s32_out[(size_t)t * N + lane + 64 * j] = s32[j];
+}
+
+__device__ __forceinline__ void seg_range(const int32_t *off, int s, int T, int &t0, int &t1) {
+    t0 = min(max(off[s], 0), T);
+    t1 = min(max(off[s + 1], 0), T);
+    if (t1 < t0) t1 = t0;
+}
+
+// Block (segment s, 64 experts): 16 token lanes x 64 experts.  Token lane r
+// adds the scores and selections of tokens t0 + r, t0 + r + 16, ...; the 16
+// partial sums are then added in r order (a fixed order).
+constexpr int kSeqRows = 16;
+__global__ __launch_bounds__(kSeqRows * kWave) void k_seq_sums(int T, int N, int K,
+                                                               const int32_t *__restrict__ off,
+                                                               const float *__restrict__ s32,
+                                                               const int32_t *__restrict__ idx,
+                                                               float *__restrict__ f_seq,
+                                                               float *__restrict__ p_seq) {
+    __shared__ double ps[kSeqRows][kWave];
+    __shared__ int cs[kSeqRows][kWave];
+    const int s = blockIdx.x;
+    const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const int e = blockIdx.y * kWave + c;
+    int t0, t1;
+    seg_range(off, s, T, t0, t1);
+    double acc = 0.0;
+    int cnt = 0;
+    if (e < N) {
+        for (int t = t0 + r; t < t1; t += kSeqRows) {
+            acc += (double)s32[(size_t)t * N + e];
+            for (int k = 0; k < K; ++k) cnt += (idx[(size_t)t * K + k] == e) ? 1 : 0;
+        }
+    }
+    ps[r][c] = acc;
+    cs[r][c] = cnt;
+    __syncthreads();
+    if (r == 0 && e < N) {
+        double p = 0.0;
+        long long n = 0;
+        for (int q = 0; q < kSeqRows; ++q) {
+            p += ps[q][c];
+            n += cs[q][c];
+        }
+        const int ts = t1 - t0;
+        f_seq[(size_t)s * N + e] = ts > 0 ? (float)((double)((long long)N * n) / (double)((long long)K * ts)) : 0.0f;
+        p_seq[(size_t)s * N + e] = ts > 0 ? (float)(p / (double)ts) : 0.0f;
+    }
+}
+
+// loss[s] = beta * sum_i f_seq[s][i] p_seq[s][i], a double tree sum.
+__global__ __launch_bounds__(256) void k_seq_loss(int N, float beta, const float *__restrict__ f_seq,
+                                                  const float *__restrict__ p_seq,
+                                                  float *__restrict__ loss) {
+    __shared__ double red[256];
+    const int s = blockIdx.x;
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < N; i += 256)
+        acc += (double)f_seq[(size_t)s * N + i] * (double)p_seq[(size_t)s * N + i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[s] = (float)((double)beta * red[0]);
+}
+
+hipError_t launch_seq_stats(const moe_config &c, const float *logits, const float *offset,
+                            const int32_t *idx, const int32_t *seg_off, int n_seg, float beta,
+                            float *scores, float *f_seq, float *p_seq, float *loss,
+                            hipStream_t s) {
+    const int J = (c.n_routed + 63) / 64;
+    dim3 grid((c.T + kSelWaves - 1) / kSelWaves), block(kSelWaves * kWave);
+#define MOE_SC(JJ)                                                                             \
+    hipLaunchKernelGGL(k_scores<JJ>, grid, block, 0, s, c.T, c.n_routed, c.scoring, logits,    \
+                       offset, scores)
+    if (J <= 1) MOE_SC(1);
+    else if (J <= 2) MOE_SC(2);
+    else if (J <= 4) MOE_SC(4);
+    else if (J <= 6) MOE_SC(6);
+    else if (J <= 8) MOE_SC(8);
+    else MOE_SC(16);
+#undef MOE_SC
+    hipLaunchKernelGGL(k_seq_sums, dim3(n_seg, J), dim3(kSeqRows * kWave), 0, s, c.T,
+                       c.n_routed, c.top_k, seg_off, scores, idx, f_seq, p_seq);
+    hipLaunchKernelGGL(k_seq_loss, dim3(n_seg), dim3(256), 0, s, c.n_routed, beta, f_seq, p_seq,
+                       loss);
+    return hipGetLastError();
+}
+
+// Device-level balance loss (DeepSeekMoE notes): thread d sums its group of
+// N / n_dev experts in index order; the loss adds the groups in order.
+__global__ __launch_bounds__(64) void k_device_stats(int N, int n_dev, float alpha2,
+                                                     const float *__restrict__ f,
+                                                     const float *__restrict__ P,
+                                                     float *__restrict__ f_dev,
+                                                     float *__restrict__ P_dev,
+                                                     float *__restrict__ loss) {
+    const int gsz = N / n_dev;
+    double raw = 0.0;
+    for (int d0 = 0; d0 < n_dev; d0 += 64) {
+        const int d = d0 + (int)threadIdx.x;
+        double fd = 0.0, pd = 0.0;
+        if (d < n_dev) {
+            for (int j = d * gsz; j < (d + 1) * gsz; ++j) {
+                fd += (double)f[j];
+                pd += (double)P[j];
+            }
+            fd /= (double)gsz;
+            f_dev[d] = (float)fd;
+            P_dev[d] = (float)pd;
+        }
+        // fixed-order sum of the 64 products of this chunk (lane 0 adds them)
+        const double prod = (d < n_dev) ? fd * pd : 0.0;
+        for (int q = 0; q < 64; ++q) {
+            const double v = __shfl(prod, q, kWave);
+            if (d0 + q < n_dev) raw += v;
+        }
+    }
+    if (loss && threadIdx.x == 0) loss[0] = (float)((double)alpha2 * raw);
+}
+
+hipError_t launch_device_stats(const moe_config &c, const float *f, const float *P, int n_dev,
+                               float alpha2, float *f_dev, float *P_dev, float *loss,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(k_device_stats, dim3(1), dim3(64), 0, s, c.n_routed, n_dev, alpha2, f, P,
+                       f_dev, P_dev, loss);
+    return hipGetLastError();
+}
+
+// Aux-loss-free bias update (V4 book ch. 02 sec. 3, V3):
+// b_i += alpha (K'/N' - c_i / n_tok), in double, rounded once.
+__global__ __launch_bounds__(256) void k_bias_update(int N, int K, long long n_tok, float alpha,
+                                                     const int32_t *__restrict__ c,
+                                                     float *__restrict__ b) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N) return;
+    const double target = (double)K / (double)N;
+    const double share = (double)c[i] / (double)n_tok;
+    b[i] = (float)((double)b[i] + (double)alpha * (target - share));
+}
+
+hipError_t launch_bias_update(const moe_config &c, const int32_t *counts, long long n_tok,
+                              float alpha, float *bias, hipStream_t s) {
+    hipLaunchKernelGGL(k_bias_update, dim3((c.n_routed + 255) / 256), dim3(256), 0, s, c.n_routed,
+                       c.top_k, n_tok, alpha, counts, bias);
+    return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void k_hash_route(int T, int N, const uint32_t *__restrict__ tid,

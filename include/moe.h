@@ -83,6 +83,14 @@ typedef struct {
                             sec. 1); 0: g = s (top-k gate equation)           */
     int32_t dtype;       /* MOE_F32 or MOE_BF16                               */
     uint32_t flags;      /* MOE_LOGITS_IN | MOE_LOGITS_OUT                    */
+    int32_t n_groups;    /* node-limited routing (V4 book ch. 02 sec. 4, V3's
+                            limit of M nodes per token): the N' experts form
+                            n_groups contiguous groups of N'/n_groups; 0 = no
+                            limit.  1..64, a divisor of N'; not under HASH    */
+    int32_t topk_groups; /* M: groups a token may draw its K' experts from;
+                            1..n_groups with M * N'/n_groups >= K'.  The pages
+                            give no ranking rule: a group ranks by its best
+                            selection key (ties: lower group index)         */
 } moe_config;
 
 /* Which workspace a size query is for. */
@@ -90,6 +98,7 @@ typedef struct {
 #define MOE_WS_FORWARD 1  /* scratch of moe_forward                             */
 #define MOE_WS_PSTAT 2    /* the p_partial buffer moe_route fills for
                              moe_balance_stats                                  */
+#define MOE_WS_SEQSTAT 3  /* scratch of moe_seq_balance_stats                   */
 
 /* Bytes of the requested buffer for this config; 0 if the config is invalid
  * or unsupported. */
@@ -108,7 +117,9 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which);
  *           load-balancing section) -- else key = l (every score function is
  *           increasing, so this is the score order)
  *   topk_idx[t] = the K' experts with the largest key, larger key first,
- *           the smaller expert index first among equal keys
+ *           the smaller expert index first among equal keys; with
+ *           cfg->n_groups > 0, only experts of the cfg->topk_groups groups
+ *           whose best key ranks highest (ties: lower group index) compete
  *   topk_w[t][k] = s[idx]  or  s[idx] / sum_k' s[idx_k'] (renorm; double sum
  *           in k order, rounded once)
  *   expert_counts[i] = #{(t, k) : topk_idx[t][k] == i}  (overwritten)
@@ -185,6 +196,65 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx,
 int moe_balance_stats(const moe_config *cfg, const int32_t *expert_counts,
                       const void *p_partial, float alpha1, float *f, float *P,
                       float *loss, void *stream);
+
+/*
+ * moe_seq_balance_stats -- in-sequence balance statistics (DeepSeek-V4 book
+ * ch. 02 sec. 3, change 2: L_seq = beta * sum_i f_i^seq p_i^seq).
+ *
+ * The batch's tokens are cut into n_seg segments (sequences): segment s
+ * holds tokens seg_offsets[s] .. seg_offsets[s+1]-1.  Per segment:
+ *   f_seq[s][i] = N' / (K' T_s) * #{(t, k) : t in s, topk_idx[t][k] == i}
+ *                 (the DeepSeekMoE notes' f_i normalisation; computed in
+ *                 double, rounded once)
+ *   p_seq[s][i] = (1/T_s) sum_{t in s} s_{i,t}, s the raw score (no bias)
+ *                 recomputed from `logits` exactly as moe_route computes it
+ *                 (double sum, rounded once)
+ *   loss_seq[s] = beta * sum_i f_seq[s][i] p_seq[s][i] (double, rounded once)
+ * An empty segment gives zeros.
+ * Arguments
+ *   logits      [T][N'] fp32, the raw x W_g^T (as moe_route's MOE_LOGITS_OUT)
+ *   logit_offset [N'] fp32 or NULL, as passed to moe_route
+ *   topk_idx    [T][K'] int32 from moe_route (ids outside [0, N') ignored)
+ *   seg_offsets [n_seg + 1] int32 device array, non-decreasing, from 0 to
+ *               at most T (values are clamped to [0, T]; a decreasing pair
+ *               is an empty segment)
+ *   f_seq, p_seq [n_seg][N'] fp32 out;  loss_seq [n_seg] fp32 out
+ *   workspace   >= moe_workspace_bytes(cfg, MOE_WS_SEQSTAT) bytes
+ * Errors: INVALID_ARG for a NULL pointer, n_seg < 1, or HASH routing (no
+ * scores); WORKSPACE; HIP.
+ */
+int moe_seq_balance_stats(const moe_config *cfg, const float *logits,
+                          const float *logit_offset, const int32_t *topk_idx,
+                          const int32_t *seg_offsets, int32_t n_seg, float beta,
+                          float *f_seq, float *p_seq, float *loss_seq,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * moe_device_balance_stats -- device-level balance loss of the DeepSeekMoE
+ * notes: the routed experts split into n_dev groups E_d (contiguous runs of
+ * N'/n_dev experts, the experts one device holds),
+ *   f_dev[d] = (1/|E_d|) sum_{j in E_d} f[j],   P_dev[d] = sum_{j in E_d} P[j],
+ *   loss[0]  = alpha2 * sum_d f_dev[d] P_dev[d]
+ * each a double sum in index order, rounded once.  f, P: [N'] fp32 as
+ * written by moe_balance_stats.  f_dev, P_dev: [n_dev] fp32 out; loss: [1]
+ * fp32 out or NULL.
+ * Errors: INVALID_ARG for a NULL pointer, n_dev < 1 or N' % n_dev != 0; HIP.
+ */
+int moe_device_balance_stats(const moe_config *cfg, const float *f, const float *P,
+                             int32_t n_dev, float alpha2, float *f_dev, float *P_dev,
+                             float *loss, void *stream);
+
+/*
+ * moe_bias_update -- the aux-loss-free bias update of V3 (DeepSeek-V4 book
+ * ch. 02 sec. 3):  b_i <- b_i + alpha * (K'/N' - c_i / n_tokens), where c_i
+ * are the expert counts accumulated over a window of n_tokens tokens (one
+ * batch: moe_route's expert_counts and T).  K'/N' is the uniform share; the
+ * update is evaluated in double and rounded once to fp32, in place.
+ * Arguments: expert_counts [N'] int32; bias [N'] fp32 in/out.
+ * Errors: INVALID_ARG for a NULL pointer or n_tokens < 1; HIP.
+ */
+int moe_bias_update(const moe_config *cfg, const int32_t *expert_counts, int64_t n_tokens,
+                    float alpha, float *bias, void *stream);
 
 /* Human-readable text of a status code (static storage; for MOE_ERR_HIP the
  * text of the last HIP error seen by this thread). */

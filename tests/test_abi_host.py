@@ -66,6 +66,12 @@ BAD_CONFIGS = [
     (dict(d_ff=96), B.MOE_ERR_UNSUPPORTED),
     (dict(d_ff_shared=80), B.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 20, top_k=8), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_groups=3, topk_groups=1), B.MOE_ERR_INVALID_ARG),      # 64 % 3
+    (dict(n_groups=8, topk_groups=0), B.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=8, topk_groups=9), B.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=16, topk_groups=1), B.MOE_ERR_INVALID_ARG),     # 1 * 4 < K' = 7
+    (dict(n_groups=0, topk_groups=2), B.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=128, topk_groups=8, n_routed=128), B.MOE_ERR_INVALID_ARG),  # > 64 groups
 ]
 
 
@@ -168,3 +174,44 @@ def test_status_strings(L):
     assert B.status_string(12345) == "unknown status"
     with pytest.raises(B.MoeError):
         B._check(B.MOE_ERR_INVALID_ARG, "x")
+
+
+def test_grouped_routing_config_is_accepted(L):
+    c = cfg_of("v3_prefill", n_groups=8, topk_groups=4)
+    assert L.moe_workspace_bytes(ctypes.byref(c), B.WS_ROUTE) > 0
+    h = cfg_of("v4_hash", n_groups=32, topk_groups=4)
+    assert L.moe_workspace_bytes(ctypes.byref(h), B.WS_ROUTE) == 0    # no groups under hash
+
+
+def test_seq_stats_argument_errors(L):
+    c = cfg_of("v3_prefill")
+    f = L.moe_seq_balance_stats
+    ok = [P, None, P, P, 2, ctypes.c_float(1e-4), P, P, P, P, 1 << 40, None]
+    assert B.workspace_bytes(c, B.WS_SEQSTAT) >= CONFIGS["v3_prefill"].T * 256 * 4
+    for i in (0, 2, 3, 6, 7, 8, 9):               # logits, idx, offsets, outputs, workspace
+        a = list(ok)
+        a[i] = None
+        assert f(ctypes.byref(c), *a) == B.MOE_ERR_INVALID_ARG, i
+    a = list(ok)
+    a[4] = 0                                       # no segment
+    assert f(ctypes.byref(c), *a) == B.MOE_ERR_INVALID_ARG
+    a = list(ok)
+    a[10] = 16
+    assert f(ctypes.byref(c), *a) == B.MOE_ERR_WORKSPACE
+    h = cfg_of("v4_hash")
+    assert f(ctypes.byref(h), *ok) == B.MOE_ERR_INVALID_ARG    # no scores under hash
+
+
+def test_device_stats_and_bias_update_argument_errors(L):
+    c = cfg_of("v3_prefill")
+    d = L.moe_device_balance_stats
+    a2 = ctypes.c_float(0.05)
+    assert d(ctypes.byref(c), None, P, 8, a2, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert d(ctypes.byref(c), P, P, 0, a2, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert d(ctypes.byref(c), P, P, 3, a2, P, P, P, None) == B.MOE_ERR_INVALID_ARG   # 256 % 3
+    assert d(ctypes.byref(c), P, P, 8, a2, None, P, P, None) == B.MOE_ERR_INVALID_ARG
+    u = L.moe_bias_update
+    al = ctypes.c_float(1e-3)
+    assert u(ctypes.byref(c), None, 8192, al, P, None) == B.MOE_ERR_INVALID_ARG
+    assert u(ctypes.byref(c), P, 0, al, P, None) == B.MOE_ERR_INVALID_ARG
+    assert u(ctypes.byref(c), P, 8192, al, None, None) == B.MOE_ERR_INVALID_ARG

@@ -17,6 +17,9 @@ workload.  Other modes:
                         WRITE_SIZE; their output folders DIR/fetch, DIR/write)
                         of `bench.py --pmc-run` into a traffic record under
                         profiles/.
+    --extras            one JSON line timing node-limited routing, the
+                        in-sequence and device-level statistics and the
+                        bias update on the workload's inputs.
 """
 from __future__ import annotations
 
@@ -85,6 +88,9 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a calibration copy plus a few steps")
     ap.add_argument("--pmc-summary", default=None)
+    ap.add_argument("--extras", action="store_true",
+                    help="time the entry points beyond the layer step (node-limited routing, "
+                         "in-sequence and device-level statistics, bias update) instead")
     return ap.parse_args(argv)
 
 
@@ -216,6 +222,88 @@ def pmc_summary(out_dir: str, workload: str, stage: str = "gate_up"):
     print(json.dumps({"traffic_bytes_per_launch": traffic, "record": traffic_record_path(workload, stage)}))
 
 
+def time_calls(fn, reps=50):
+    """Average ms of fn() over reps calls, HIP events on torch's current
+    stream (the binding launches on that stream)."""
+    import torch
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def extras(cfg):
+    """One JSON line timing the entry points beyond the layer step on the
+    workload's own inputs: node-limited routing (8 groups, M = 4) against
+    plain routing, moe_seq_balance_stats over 8 equal segments,
+    moe_device_balance_stats over 8 devices, moe_bias_update."""
+    import torch
+    from fine_grained_moe_router_amd import binding as B
+    from fine_grained_moe_router_amd.synth import make_inputs
+
+    inp = make_inputs(cfg, "cuda", experts=False)
+    T, N, K = cfg.T, cfg.n_routed, cfg.top_k
+    grouped = cfg.with_(n_groups=8, topk_groups=4)
+    res = {}
+    for name, c in (("route_plain", cfg), ("route_node_limited", grouped)):
+        ws = B.alloc_workspace(B.make_config(c), B.WS_ROUTE, "cuda")
+        out = {"idx": torch.empty((T, K), dtype=torch.int32, device="cuda"),
+               "w": torch.empty((T, K), dtype=torch.float32, device="cuda"),
+               "counts": torch.empty(N, dtype=torch.int32, device="cuda"),
+               "pstat": torch.empty(B.workspace_bytes(B.make_config(c), B.WS_PSTAT),
+                                    dtype=torch.uint8, device="cuda")}
+
+        def call(c=c, ws=ws, out=out):
+            B.route(c, x=inp.x, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias, out=out,
+                    workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        B.profile_enable(400)
+        n = 50
+        for _ in range(n):
+            call()
+        torch.cuda.synchronize()
+        st = B.profile_collect()
+        res[name] = {"select_us": st["select"]["ms"] / n * 1e3,
+                     "router_gemm_us": st["router_gemm"]["ms"] / n * 1e3}
+    sel = res["route_node_limited"]["select_us"]
+    # the select stage reads the logits and writes K' (index, gate) pairs per token
+    sel_bytes = T * N * 4 + T * K * 8
+    res["route_node_limited"].update(bound="latency", bytes=sel_bytes,
+                                     gbs=sel_bytes / (sel * 1e-6) / 1e9)
+
+    r = B.route(cfg, x=inp.x, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias,
+                logits_out=True)
+    S = 8
+    segs = torch.tensor([i * T // S for i in range(S + 1)], dtype=torch.int32, device="cuda")
+    ws = B.alloc_workspace(B.make_config(cfg), B.WS_SEQSTAT, "cuda")
+    outs = {"f_seq": torch.empty((S, N), device="cuda"), "p_seq": torch.empty((S, N), device="cuda"),
+            "loss": torch.empty(S, device="cuda")}
+    ms = time_calls(lambda: B.seq_balance_stats(cfg, r["logits"], r["idx"], segs, 1e-4,
+                                                offset=inp.offset, out=outs, workspace=ws))
+    alg = T * N * 4 + T * K * 4 + 2 * S * N * 4 + S * 4      # logits, idx in; f, p, loss out
+    res["seq_balance_stats"] = {"segments": S, "us": ms * 1e3, "bound": "hbm",
+                                "algorithmic_bytes": alg, "gbs": alg / (ms * 1e-3) / 1e9,
+                                "frac": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                "implementation_bytes": alg + 2 * T * N * 4}
+    f, P, _ = B.balance_stats(cfg, r["counts"], r["pstat"])
+    ms = time_calls(lambda: B.device_balance_stats(cfg, f, P, 8, 0.05))
+    res["device_balance_stats"] = {"devices": 8, "us": ms * 1e3, "bound": "latency"}
+    bias = inp.bias.clone() if inp.bias is not None else torch.zeros(N, device="cuda")
+    ms = time_calls(lambda: B.bias_update(cfg, r["counts"], T, 1e-3, bias))
+    res["bias_update"] = {"us": ms * 1e3, "bound": "latency"}
+    print(json.dumps({"mode": "extras", "workload": cfg.name, "T": T, "n_routed": N,
+                      "top_k": K, "entries": res}))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -234,6 +322,8 @@ def main(argv=None):
     cfg = CONFIGS[args.workload]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()   # fails loudly if the HIP library is not built
+    if args.extras:
+        return extras(cfg)
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     layer = Layer(cfg)
     torch.cuda.synchronize()

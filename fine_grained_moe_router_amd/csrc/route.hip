@@ -384,8 +384,10 @@ __device__ __forceinline__ void seg_range(const int32_t *off, int s, int T, int 
 }
 
 // Block (segment s, 64 experts): 16 token lanes x 64 experts.  Token lane r
-// adds the scores and selections of tokens t0 + r, t0 + r + 16, ...; the 16
-// partial sums are then added in r order (a fixed order).
+// adds the scores of tokens t0 + r, t0 + r + 16, ...; the 16 partial sums
+// are then added in r order (a fixed order).  Selections are counted in an
+// LDS histogram of the block's 64 experts (integer adds: order-free): lane
+// k < K' of token lane r reads slot k of the token's selection.
 constexpr int kSeqRows = 16;
 __global__ __launch_bounds__(kSeqRows * kWave) void k_seq_sums(int T, int N, int K,
                                                                const int32_t *__restrict__ off,
@@ -394,30 +396,31 @@ __global__ __launch_bounds__(kSeqRows * kWave) void k_seq_sums(int T, int N, int
                                                                float *__restrict__ f_seq,
                                                                float *__restrict__ p_seq) {
     __shared__ double ps[kSeqRows][kWave];
-    __shared__ int cs[kSeqRows][kWave];
+    __shared__ int hist[kWave];
     const int s = blockIdx.x;
     const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
-    const int e = blockIdx.y * kWave + c;
+    const int e0 = blockIdx.y * kWave;
+    const int e = e0 + c;
+    if (threadIdx.x < kWave) hist[threadIdx.x] = 0;
+    __syncthreads();
     int t0, t1;
     seg_range(off, s, T, t0, t1);
     double acc = 0.0;
-    int cnt = 0;
-    if (e < N) {
-        for (int t = t0 + r; t < t1; t += kSeqRows) {
-            acc += (double)s32[(size_t)t * N + e];
-            for (int k = 0; k < K; ++k) cnt += (idx[(size_t)t * K + k] == e) ? 1 : 0;
+    const float *col = s32 + (e < N ? e : 0);
+#pragma unroll 8
+    for (int t = t0 + r; t < t1; t += kSeqRows) {
+        if (e < N) acc += (double)col[(size_t)t * N];
+        if (c < K) {
+            const int sel = idx[(size_t)t * K + c] - e0;
+            if (sel >= 0 && sel < kWave) atomicAdd(&hist[sel], 1);
         }
     }
     ps[r][c] = acc;
-    cs[r][c] = cnt;
     __syncthreads();
     if (r == 0 && e < N) {
         double p = 0.0;
-        long long n = 0;
-        for (int q = 0; q < kSeqRows; ++q) {
-            p += ps[q][c];
-            n += cs[q][c];
-        }
+        for (int q = 0; q < kSeqRows; ++q) p += ps[q][c];
+        const long long n = hist[c];
         const int ts = t1 - t0;
         f_seq[(size_t)s * N + e] = ts > 0 ? (float)((double)((long long)N * n) / (double)((long long)K * ts)) : 0.0f;
         p_seq[(size_t)s * N + e] = ts > 0 ? (float)(p / (double)ts) : 0.0f;
@@ -582,8 +585,10 @@ __global__ __launch_bounds__(1024) void k_balance(int T, int N, int K, const int
     const int G = 1024 / Np;
     const int e = threadIdx.x % Np, r = threadIdx.x / Np;
     double s = 0.0;
-    if (part && e < N)
+    if (part && e < N) {
+#pragma unroll 8
         for (int b = r; b < nblk; b += G) s += part[(size_t)b * N + e];
+    }
     red[threadIdx.x] = s;
     __syncthreads();
     double acc = 0.0;

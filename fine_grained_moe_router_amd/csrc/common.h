@@ -52,6 +52,8 @@ struct FwdLayout {
     size_t off_meta;    // int32 meta block (see MetaIdx)
     size_t off_perm;    // int32 [T*K']: pair id at each expert-ordered row
     size_t off_gsort;   // fp32 [T*K']: gate of each expert-ordered row
+    size_t off_rtg;     // int32 [max_row_tiles]: group of each 256-row tile
+    int max_row_tiles;  // bound on the row tiles of all groups
     size_t off_zr;      // [T*K'][d_ff] dtype: routed hidden activations
     size_t off_zs;      // [T][K_s*d_ff_shared] dtype: shared hidden activations
     size_t off_yr;      // fp32 [T*K'][d]: gate-scaled routed outputs, pair order
@@ -100,6 +102,7 @@ struct GroupedArgs {
     // work queues of the bf16 kernels: row-tile prefix sums, per-XCD
     // row-tile ranges and item counters, column tiles per row tile
     const int32_t *mt_base, *xsplit;
+    const int32_t *rtg;       // group of each row tile
     int32_t *queue;
     int nt_routed, nt_shared;
     const int32_t *perm;      // pair id per expert-ordered row

@@ -106,20 +106,19 @@ __device__ __forceinline__ int wave_frags(int nrows) {
 // (row tile, column tile) pairs of that range.  The blocks of the XCD pull
 // items in order from the XCD's counter, so the blocks busy at any moment
 // hold consecutive items and share their operands through the XCD's L2;
-// pulling also balances tiles of unequal cost.  Item order within a group:
-// a routed expert with at most kColMajorRows row tiles in the range lists
-// them row tile fastest -- its row tiles that stream the same weight tile
-// start together -- while a longer group (the shared experts, a heavily
-// loaded expert) lists column tile fastest, so the gang of column tiles on
-// one row tile shares its token rows.
+// pulling also balances tiles of unequal cost (a block whose XCD has no
+// items left takes them from the other XCDs' queues).  Item order within a
+// group: a routed expert with at most kColMajorRows row tiles in the range
+// lists them row tile fastest -- its row tiles that stream the same weight
+// tile start together -- while a longer group (the shared experts, a
+// heavily loaded expert) lists column tile fastest, so the gang of column
+// tiles on one row tile shares its token rows.
 constexpr int kColMajorRows = 4;
 
 struct XcdQueue {
     int m0, ms, m1, ntr, nts, nr_items, total;
-    int32_t *ctr;
 };
-__device__ __forceinline__ XcdQueue xcd_queue(const GroupedArgs &a) {
-    const int x = blockIdx.x % kXcds;
+__device__ __forceinline__ XcdQueue xcd_queue(const GroupedArgs &a, int x) {
     XcdQueue q;
     q.m0 = a.xsplit[x];
     q.m1 = a.xsplit[x + 1];
@@ -130,7 +129,6 @@ __device__ __forceinline__ XcdQueue xcd_queue(const GroupedArgs &a) {
     q.nts = a.nt_shared;
     q.nr_items = (q.ms - q.m0) * q.ntr;
     q.total = q.nr_items + (q.m1 - q.ms) * q.nts;
-    q.ctr = a.queue + x;
     return q;
 }
 // Item -> (row tile m, column tile j).  The routed items of a group with
@@ -140,7 +138,7 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
     int lo, r, local, nt;
     if (item < q.nr_items) {
         nt = q.ntr;
-        const int g = find_group(a.mt_base, a.n_routed, q.m0 + item / nt);
+        const int g = a.rtg[q.m0 + item / nt];
         lo = max(a.mt_base[g], q.m0);
         r = min(a.mt_base[g + 1], q.ms) - lo;
         local = item - (lo - q.m0) * nt;
@@ -160,35 +158,99 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
     }
 }
 
-// The item a block works on next is pulled by thread 0 when a tile starts
-// and handed to the other threads through one LDS word in the second A
+// Tickets.  When a tile starts, thread 0 takes a ticket from the counter of
+// queue (x + k) % 8 (x: the block's XCD; k: thread 0's state, 0 while the
+// XCD's own range lasts) without waiting for it.  Right after the K loop it
+// resolves the ticket: one past that queue's end moves it on to the next
+// queue -- work stealing once the XCD's own range is drained -- until it
+// holds an item or every queue is drained.  The item (queue << 24 | index,
+// or -1) reaches the other threads through one LDS word in the second A
 // stage: after the K loop no wave reads that stage, and the next tile first
 // writes it after the top barrier of its first k-tile, which every wave
 // reaches only after it has read the word.
+constexpr int kItemBits = 24;
 constexpr int kQueueSlotOffset = PipeTile::A_STAGE;
 static_assert(PipeTile::A_STAGES == 2, "queue slot lives in the second A stage");
 
-__device__ __forceinline__ int pull_item(int32_t *ctr) {
-    return (threadIdx.x == 0) ? atomicAdd(ctr, 1) : 0;
+__device__ __forceinline__ int take_ticket(const GroupedArgs &a, int k) {
+    return (threadIdx.x == 0 && k < kXcds) ? atomicAdd(a.queue + (blockIdx.x + k) % kXcds, 1) : 0;
 }
-// Called by every thread right after the K loop of a tile.
-__device__ __forceinline__ int publish_item(char *lds, int next) {
+__device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int &k, int ticket) {
+    const int x = blockIdx.x % kXcds;
+    while (k < kXcds) {
+        const int y = (x + k) % kXcds;
+        if (ticket < xcd_queue(a, y).total) return (y << kItemBits) | ticket;
+        if (++k < kXcds) ticket = atomicAdd(a.queue + (x + k) % kXcds, 1);
+    }
+    return -1;
+}
+// Called by every thread right after the K loop of a tile (and once before
+// the first tile).
+__device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int &k, int ticket) {
     int32_t *slot = (int32_t *)(lds + kQueueSlotOffset);
-    if (threadIdx.x == 0) *slot = next;
+    if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
     lds_barrier();
     return __builtin_amdgcn_readfirstlane(*slot);
+}
+__device__ __forceinline__ void item_tile(const GroupedArgs &a, int item, int &m, int &j) {
+    const XcdQueue q = xcd_queue(a, item >> kItemBits);
+    queue_item(a, q, item & ((1 << kItemBits) - 1), m, j);
+}
+
+// 4x4 transpose across the four lanes of a quad (lanes 4q .. 4q+3): on
+// entry lane p holds column p of the block (v[r] = M[r][p]), on exit row p
+// (v[c] = M[p][c]).  Two exchange stages, lane ^ 1 then lane ^ 2, with DPP
+// quad permutations.
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int p) {
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+        const float got = quad_xor1((p & 1) ? v[k] : v[k + 1]);
+        if (p & 1) v[k] = got;
+        else v[k + 1] = got;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float got = quad_xor2((p & 2) ? v[k] : v[k + 2]);
+        if (p & 2) v[k] = got;
+        else v[k + 2] = got;
+    }
+}
+
+// Epilogue coordinates after quad_transpose of accumulator registers
+// 4 rq .. 4 rq + 3 of fragment i: the lane's output row, and the first of
+// its four consecutive columns relative to the fragment's column block.
+__device__ __forceinline__ int quad_row(int tid, int i, int rq) {
+    const int lane = tid & 63;
+    const int wm = (tid >> 6) & 1;
+    return PipeTile::a_row(wm, i) + rq * 8 + (lane >> 5) * 4 + (lane & 3);
+}
+__device__ __forceinline__ int quad_col(int tid) { return (tid & 31) & ~3; }
+
+__device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    return o;
 }
 
 // One gate/up tile whose wave computes NF row fragments.
 template <int NF>
 __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                             const OperandRows &rows, int zc0, int zw,
-                                            size_t rbase, int next) {
+                                            size_t rbase, int ticket, int &k) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
     pipe_gemm_nf<true, NF>(lds, rows, a.d, 0, 1, 0, acc);
-    const int item = publish_item(lds, next);
+    const int item = publish_item(lds, a, k, ticket);
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
     // split group the residual z - hi goes, rounded, zw columns further.
+    // Four rows' z of one column are transposed across a lane quad so each
+    // lane stores four consecutive columns of one row (8 bytes).
     uint16_t *zout = (uint16_t *)(tj.shared ? a.zs : a.zr);
     const int split = tj.shared ? a.split_s : a.split_r;
     const size_t zstride = (size_t)zw * (split ? 2 : 1);
@@ -197,19 +259,30 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int tid = opaque_tid();
-            const int col = zc0 + pipe_out_col<true>(tid, h);
-            if (col >= zw) continue;
+            const int col = zc0 + (pipe_out_col<true>(tid, h) & ~3);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = pipe_out_row(tid, i, r);
-                if (row < tj.nrows) {
-                    const float ga = acc[i][h][r];
-                    const float up = acc[i][h + 2][r];
-                    const float z = ga / (1.0f + __expf(-ga)) * up;
-                    const uint16_t hi = f32_to_bf16(z);
+            for (int rq = 0; rq < 4; ++rq) {
+                float z[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float ga = acc[i][h][4 * rq + q];
+                    const float up = acc[i][h + 2][4 * rq + q];
+                    z[q] = ga / (1.0f + __expf(-ga)) * up;
+                }
+                quad_transpose(z, tid & 3);
+                const int row = quad_row(tid, i, rq);
+                if (row < tj.nrows && col < zw) {
                     uint16_t *dst = zout + (rbase + row) * zstride + col;
-                    dst[0] = hi;
-                    if (split) dst[zw] = f32_to_bf16(z - bf16_to_f32(hi));
+                    const uint2 hi = pack_bf16x4(z);
+                    *(uint2 *)dst = hi;
+                    if (split) {
+                        float lo[4];
+                        lo[0] = z[0] - bf16_to_f32((uint16_t)(hi.x & 0xFFFF));
+                        lo[1] = z[1] - bf16_to_f32((uint16_t)(hi.x >> 16));
+                        lo[2] = z[2] - bf16_to_f32((uint16_t)(hi.y & 0xFFFF));
+                        lo[3] = z[3] - bf16_to_f32((uint16_t)(hi.y >> 16));
+                        *(uint2 *)(dst + zw) = pack_bf16x4(lo);
+                    }
                 }
             }
             // keep one fragment pair live at a time
@@ -221,7 +294,7 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
 
 __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm) {
     TileJob t;
-    t.g = find_group(a.mt_base, a.G, m);
+    t.g = a.rtg[m];
     t.i = m - a.mt_base[t.g];
     t.j = 0;
     t.row0 = t.i * bm;
@@ -231,7 +304,7 @@ __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm)
 }
 
 __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                            int next) {
+                                            int ticket, int &k) {
     using P = PipeTile;
     const int fsum = a.n_shared * a.fs;
     const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
@@ -264,25 +337,25 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
     }
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
     switch (wave_frags(tj.nrows)) {
-        case 4: return gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase, next);
-        case 3: return gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase, next);
-        case 2: return gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase, next);
-        case 1: return gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase, next);
-        default: return gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase, next);
+        case 4: return gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase, ticket, k);
+        case 3: return gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase, ticket, k);
+        case 2: return gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase, ticket, k);
+        case 1: return gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase, ticket, k);
+        default: return gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase, ticket, k);
     }
 }
 
 __global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
-    const XcdQueue q = xcd_queue(a);
-    int item = publish_item(lds, pull_item(q.ctr));
-    while (item < q.total) {
-        const int next = pull_item(q.ctr);
+    int k = 0;
+    int item = publish_item(lds, a, k, take_ticket(a, k));
+    while (item >= 0) {
+        const int ticket = take_ticket(a, k);
         int m, j;
-        queue_item(a, q, item, m, j);
+        item_tile(a, item, m, j);
         TileJob tj = row_tile(a, m, PipeTile::BM);
         tj.j = j;
-        item = gate_up_body(a, tj, lds, next);
+        item = gate_up_body(a, tj, lds, ticket, k);
     }
 }
 
@@ -300,7 +373,7 @@ static_assert(PipeTile::B_STAGES == 3, "row info lives in the third B stage");
 template <int NF>
 __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                          const OperandRows &rows, int K, int split, int n0,
-                                         int my_pair, float my_gate, int next) {
+                                         int my_pair, float my_gate, int ticket, int &k) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
     if (tj.shared)
         pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, acc);
@@ -308,27 +381,36 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
         pipe_gemm_nf<false, NF>(lds, rows, K, split ? a.f : 0, 1, 0, acc);
     int2 *info = (int2 *)(lds + kRowInfoOffset);
     if (!tj.shared) info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
-    const int item = publish_item(lds, next);   // its barrier also publishes info
+    const int item = publish_item(lds, a, k, ticket);   // its barrier also publishes info
+    // Four rows of one column are transposed across a lane quad: each lane
+    // then stores four consecutive fp32 columns of one row (16 bytes).
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int rq = 0; rq < 4; ++rq) {
             const int tid = opaque_tid();
-            const int row = pipe_out_row(tid, i, r);
-            if (row >= tj.nrows) continue;
-            float *dst;
+            const int row = quad_row(tid, i, rq);
+            float *dst = nullptr;
             float gate = 1.0f;
-            if (tj.shared) {
-                dst = a.ys + (size_t)(tj.row0 + row) * a.d;
-            } else {
-                const int2 v = info[row];
-                gate = __int_as_float(v.y);
-                dst = a.yr + (size_t)v.x * a.d;
+            if (row < tj.nrows) {
+                if (tj.shared) {
+                    dst = a.ys + (size_t)(tj.row0 + row) * a.d;
+                } else {
+                    const int2 v = info[row];
+                    gate = __int_as_float(v.y);
+                    dst = a.yr + (size_t)v.x * a.d;
+                }
             }
 #pragma unroll
             for (int j = 0; j < PipeTile::FN; ++j) {
-                const int col = n0 + pipe_out_col<false>(tid, j);
-                if (col < a.d) dst[col] = gate * acc[i][j][r];
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * rq + q];
+                quad_transpose(v, tid & 3);
+                const int col = n0 + (pipe_out_col<false>(tid, j) & ~3);
+                if (dst && col < a.d)
+                    *(float4 *)(dst + col) = make_float4(gate * v[0], gate * v[1], gate * v[2],
+                                                         gate * v[3]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -337,7 +419,7 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
 }
 
 __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                         int next) {
+                                         int ticket, int &k) {
     using P = PipeTile;
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
@@ -371,25 +453,25 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
         my_gate = a.gsort[rbase + threadIdx.x];
     }
     switch (wave_frags(tj.nrows)) {
-        case 4: return down_tile<4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
-        case 3: return down_tile<3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
-        case 2: return down_tile<2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
-        case 1: return down_tile<1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
-        default: return down_tile<0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, next);
+        case 4: return down_tile<4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, ticket, k);
+        case 3: return down_tile<3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, ticket, k);
+        case 2: return down_tile<2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, ticket, k);
+        case 1: return down_tile<1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, ticket, k);
+        default: return down_tile<0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, ticket, k);
     }
 }
 
 __global__ __launch_bounds__(PipeTile::NT) void k_down_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
-    const XcdQueue q = xcd_queue(a);
-    int item = publish_item(lds, pull_item(q.ctr));
-    while (item < q.total) {
-        const int next = pull_item(q.ctr);
+    int k = 0;
+    int item = publish_item(lds, a, k, take_ticket(a, k));
+    while (item >= 0) {
+        const int ticket = take_ticket(a, k);
         int m, j;
-        queue_item(a, q, item, m, j);
+        item_tile(a, item, m, j);
         TileJob tj = row_tile(a, m, PipeTile::BM);
         tj.j = j;
-        item = down_body(a, tj, lds, next);
+        item = down_body(a, tj, lds, ticket, k);
     }
 }
 

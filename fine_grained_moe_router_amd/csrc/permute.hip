@@ -43,6 +43,12 @@ FwdLayout fwd_layout(const moe_config &c) {
     o = align256(o + P * 4);
     L.off_gsort = o;
     o = align256(o + P * 4);
+    // row tiles: sum over groups of ceil(rows / bm1) <= P / bm1 + G, plus the
+    // shared group's T / bm1 + 1
+    const TileShape ts = tile_shape(c);
+    L.max_row_tiles = (int)(P / ts.bm1) + L.G + (int)(c.T / ts.bm1) + 2;
+    L.off_rtg = o;
+    o = align256(o + (size_t)L.max_row_tiles * 4);
     L.off_zr = o;
     o = align256(o + P * c.d_ff * eb * (z_split_routed(c) ? 2 : 1));
     L.off_zs = o;
@@ -102,8 +108,9 @@ __device__ int block_excl_scan(int32_t *data, int n, int32_t *tmp) {
 // Per-XCD row-tile ranges of one GEMM, balanced by estimated cost: a row
 // tile with r valid rows costs nt (2 + ceil(r / 64)) (nt column tiles, each
 // streaming its weight tile and issuing MFMAs for ceil(r / 64) 64-row
-// slices).  Row tile m of group g starts at cost gcost_base[g] + i nt 6 (all
-// but a group's last row tile are full).  XCD x takes the row tiles whose
+// slices), with nt scaled by the group's relative K where it differs.  Row
+// tile m of group g starts at cost gcost_base[g] + i nt 6 (all but a
+// group's last row tile are full).  XCD x takes the row tiles whose
 // start cost lies in [x C / 8, (x + 1) C / 8).
 __device__ void xcd_splits(int G, const int32_t *cnt, const int32_t *mtb, const int32_t *ntg,
                            int32_t *gcost, int32_t *tmp, int32_t *out) {
@@ -143,9 +150,11 @@ __device__ void xcd_splits(int G, const int32_t *cnt, const int32_t *mtb, const 
 // computes group row counts/offsets, the tile prefix sums of both GEMMs, the
 // row-tile prefix sums and the per-XCD row-tile ranges.
 __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, int n_shared,
-                                                    int f, int fsum, int d, TileShape ts,
+                                                    int f, int fsum, int d, int split_r,
+                                                    int split_s, TileShape ts,
                                                     int32_t *__restrict__ cc,
-                                                    int32_t *__restrict__ meta) {
+                                                    int32_t *__restrict__ meta,
+                                                    int32_t *__restrict__ rtg) {
     __shared__ int32_t cnt[2048], t1[2048], t2[2048], tmp[1024];
     __shared__ int32_t mtb[2048], nt1[2048], nt2[2048], gcost[2048];
     const int G = N + (n_shared > 0 ? 1 : 0);
@@ -186,11 +195,17 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
     if (threadIdx.x == 0 && n_shared > 0) cnt[N] = T;
     __syncthreads();
     const int ntn2 = (d + ts.bn2 - 1) / ts.bn2;
+    // The down GEMM's K differs between groups (d_ff for a routed expert,
+    // K_s d_ff_s for the shared group, doubled for a (hi, lo) split): its
+    // row-tile cost scales with K relative to the routed K (capped at 64).
+    const int k_routed = f * (split_r ? 2 : 1);
+    const int k_shared = fsum * (split_s ? 2 : 1);
+    const int kfac_shared = min(64, (k_shared + k_routed - 1) / k_routed);
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
         const int c = cnt[g];
         const int width = (g < N) ? f : fsum;
         nt1[g] = (width + ts.bz1 - 1) / ts.bz1;
-        nt2[g] = ntn2;
+        nt2[g] = ntn2 * ((g < N) ? 1 : kfac_shared);
         t1[g] = ((c + ts.bm1 - 1) / ts.bm1) * nt1[g];
         t2[g] = ((c + ts.bm2 - 1) / ts.bm2) * ntn2;
         mtb[g] = (c + ts.bm1 - 1) / ts.bm1;
@@ -203,6 +218,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
     if (threadIdx.x == 0) mtb[G] = totm;
     __syncthreads();
     for (int g = threadIdx.x; g <= G; g += blockDim.x) meta[mi.mt + g] = mtb[g];
+    for (int g = threadIdx.x; g < G; g += blockDim.x)
+        for (int m = mtb[g]; m < mtb[g + 1]; ++m) rtg[m] = g;
     xcd_splits(G, cnt, mtb, nt1, gcost, tmp, meta + mi.xs1);
     xcd_splits(G, cnt, mtb, nt2, gcost, tmp, meta + mi.xs2);
     // row offsets of the routed groups (the shared group reads rows 0..T-1)
@@ -255,7 +272,9 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
     hipLaunchKernelGGL(k_perm_hist, dim3(L.n_chunks), dim3(256), (size_t)N * 4, s, P, N, L.chunk,
                        idx, cc, meta + mi.bad);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, L.n_chunks, c.T, c.n_shared,
-                       c.d_ff, c.n_shared * c.d_ff_shared, c.d_model, tile_shape(c), cc, meta);
+                       c.d_ff, c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
+                       z_split_shared(c) ? 1 : 0, tile_shape(c), cc, meta,
+                       (int32_t *)(ws + L.off_rtg));
     hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
                        L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
                        (float *)(ws + L.off_gsort));

@@ -175,11 +175,44 @@ static_assert(PipeTile::A_STAGES == 2, "queue slot lives in the second A stage")
 __device__ __forceinline__ int take_ticket(const GroupedArgs &a, int k) {
     return (threadIdx.x == 0 && k < kXcds) ? atomicAdd(a.queue + (blockIdx.x + k) % kXcds, 1) : 0;
 }
+#ifndef MOE_PAIR_WAIT
+#define MOE_PAIR_WAIT 1
+#endif
+constexpr int kPairSpin = 32;
+
+// For the first item of a row-fastest run (the row tiles of one routed
+// expert that stream the same weight tile), the number of tickets after it
+// that belong to the run; else 0.
+__device__ __forceinline__ int run_followers(const GroupedArgs &a, const XcdQueue &q, int item) {
+    if (item >= q.nr_items) return 0;
+    const int nt = q.ntr;
+    const int g = a.rtg[q.m0 + item / nt];
+    const int lo = max(a.mt_base[g], q.m0);
+    const int r = min(a.mt_base[g + 1], q.ms) - lo;
+    if (r < 2 || r > kColMajorRows) return 0;
+    const int local = item - (lo - q.m0) * nt;
+    return (local % r == 0) ? r - 1 : 0;
+}
+
 __device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int &k, int ticket) {
     const int x = blockIdx.x % kXcds;
     while (k < kXcds) {
         const int y = (x + k) % kXcds;
-        if (ticket < xcd_queue(a, y).total) return (y << kItemBits) | ticket;
+        const XcdQueue q = xcd_queue(a, y);
+        if (ticket < q.total) {
+            // The first tile of a run starts once its followers have been
+            // handed out (bounded wait): the run's tiles then stream their
+            // shared weight tile close together in time, so all but the
+            // first fetch hit the XCD's L2.
+            const int f = (MOE_PAIR_WAIT && k == 0) ? run_followers(a, q, ticket) : 0;
+            for (int it = 0; f > 0 && it < kPairSpin; ++it) {
+                if (__hip_atomic_load(a.queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >
+                    ticket + f)
+                    break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+            return (y << kItemBits) | ticket;
+        }
         if (++k < kXcds) ticket = atomicAdd(a.queue + (x + k) % kXcds, 1);
     }
     return -1;
@@ -256,17 +289,16 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
     const size_t zstride = (size_t)zw * (split ? 2 : 1);
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        {
             const int tid = opaque_tid();
-            const int col = zc0 + (pipe_out_col<true>(tid, h) & ~3);
+            const int col = zc0 + (pipe_out_col<true>(tid, 0) & ~3);
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 float z[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float ga = acc[i][h][4 * rq + q];
-                    const float up = acc[i][h + 2][4 * rq + q];
+                    const float ga = acc[i][0][4 * rq + q];   // W1 (gate) fragment
+                    const float up = acc[i][1][4 * rq + q];   // W3 (up) fragment
                     z[q] = ga / (1.0f + __expf(-ga)) * up;
                 }
                 quad_transpose(z, tid & 3);
@@ -364,7 +396,7 @@ __global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs
 // epilogue area: the third B stage, which no wave reads after the K loop and
 // which the next tile first writes after the top barrier of its first k-tile.
 constexpr int kRowInfoOffset = PipeTile::A_STAGES * PipeTile::A_STAGE + 2 * PipeTile::B_STAGE;
-static_assert(PipeTile::NT == PipeTile::BM, "one tile row per thread");
+static_assert(PipeTile::NT >= PipeTile::BM, "one tile row per thread");
 static_assert(PipeTile::B_STAGES == 3, "row info lives in the third B stage");
 
 // One down-projection tile whose wave computes NF row fragments.  Thread t
@@ -380,7 +412,8 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     else
         pipe_gemm_nf<false, NF>(lds, rows, K, split ? a.f : 0, 1, 0, acc);
     int2 *info = (int2 *)(lds + kRowInfoOffset);
-    if (!tj.shared) info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
+    if (!tj.shared && threadIdx.x < PipeTile::BM)
+        info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
     const int item = publish_item(lds, a, k, ticket);   // its barrier also publishes info
     // Four rows of one column are transposed across a lane quad: each lane
     // then stores four consecutive fp32 columns of one row (16 bytes).

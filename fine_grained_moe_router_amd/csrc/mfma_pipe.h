@@ -2,10 +2,13 @@
 // GEMMs (gfx950).
 //
 // C[256][256] = A[256][K] B[256][K]^T, both operands K-contiguous, fp32
-// accumulation with v_mfma_f32_32x32x16_bf16.  Four waves (one per SIMD),
-// 2 x 2, each owning a 128 x 128 accumulator block (256 accumulator
-// registers per lane): the largest per-wave block, so the fewest LDS and
-// L2 bytes per MFMA.
+// accumulation with v_mfma_f32_32x32x16_bf16.  Eight waves, two per SIMD,
+// in a 2 x 4 grid, each owning a 128 x 64 accumulator block (128 registers
+// per lane).  With one 128 x 128 wave per SIMD (the fewest LDS bytes per
+// MFMA) nothing hides a wave's waits on its loads, LDS reads and barriers:
+// a skeleton of this pipeline with every operand in L2 ran at 1.72 us per
+// k-tile with one wave per SIMD and 1.37 us with two (the MFMAs alone take
+// 0.85 us).
 //
 // Memory pipeline.  k-tiles of 64 values: each row contributes one whole
 // 128-byte cache line per k-tile (half-line requests halve the per-CU rate
@@ -21,9 +24,9 @@
 // HBM once, long latency) has three 32 KB stages -- its loads run two
 // k-tiles ahead -- while A (token rows, shared by the column tiles that run
 // together on one XCD and mostly served by L2) has two.  2 x 32 + 3 x 32 KB
-// is the whole 160 KB LDS.  The next k-tile's loads are spread through the
-// MFMA stream (one per group of four MFMAs), so a busy load queue never
-// holds a run of MFMAs back.
+// is the whole 160 KB LDS.  The next k-tile's loads are spread evenly
+// through the MFMA stream, so a busy load queue never holds a run of MFMAs
+// back.
 //
 // Partial row tiles: wave row wm owns the 32-row fragments 2 i + wm
 // (i < 4), so a tile with n valid rows issues MFMAs only for fragments that
@@ -35,7 +38,7 @@
 namespace moe {
 
 struct PipeTile {
-    static constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+    static constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
     static constexpr int A_STAGES = 2, B_STAGES = 3;
     static constexpr int CHUNKS = BK / 8;                  // 16-byte chunks per row
     static constexpr int A_LD = BM * CHUNKS / NT;          // global_load_lds per thread, A
@@ -43,7 +46,7 @@ struct PipeTile {
     static constexpr int A_STAGE = BM * CHUNKS * 16;       // bytes
     static constexpr int B_STAGE = BN * CHUNKS * 16;
     static constexpr int LDS_BYTES = A_STAGES * A_STAGE + B_STAGES * B_STAGE;
-    static constexpr int FM = 4, FN = 4;                   // 32x32 fragments per wave
+    static constexpr int FM = 4, FN = 2;                   // 32x32 fragments per wave
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __device__ static __forceinline__ int slot(int row, int chunk) {
@@ -57,13 +60,13 @@ struct PipeTile {
     __device__ static __forceinline__ int load_chunk(int tid) {
         return slot(load_row(tid, 0), tid % CHUNKS);   // slot() is its own inverse
     }
-    // B tile row feeding fragment j of wave column wn.  SPLIT: fragments
-    // 0,1 come from the first half (rows wn*64 + 32 j), 2,3 from the second
-    // half at the same offsets.
+    // B tile row feeding fragment j of wave column wn (0..3).  SPLIT:
+    // fragment 0 comes from the first half (rows wn*32 ..), fragment 1 from
+    // the second half at the same offset.
     template <bool SPLIT>
     __device__ static __forceinline__ int b_row(int wn, int j) {
-        if (SPLIT) return (j < 2) ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32;
-        return wn * 128 + j * 32;
+        if (SPLIT) return (j == 0) ? wn * 32 : BN / 2 + wn * 32;
+        return wn * 64 + j * 32;
     }
     // Tile row of fragment i of wave row wm.
     __device__ static __forceinline__ int a_row(int wm, int i) { return (2 * i + wm) * 32; }
@@ -160,8 +163,6 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
     constexpr int SUB = P::BK / 16;          // MFMA k-substeps per k-tile
     constexpr int SLOTS = 4 * SUB;           // MFMA groups per k-tile
     constexpr int LOADS = P::A_LD + P::B_LD;
-    static_assert(LOADS % SLOTS == 0, "load interleave");
-    constexpr int PER_SLOT = LOADS / SLOTS;
     for (int kt = 0; kt < nk; ++kt) {
         wait_vmcnt<P::B_LD>();   // A(kt) and B(kt) have landed (this thread's share)
         lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
@@ -198,9 +199,10 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
                         for (int j = 0; j < P::FN; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                 a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+                // this group's share of the next loads, A loads first, then B
 #pragma unroll
-                for (int u = 0; u < PER_SLOT; ++u) {
-                    const int n = (s * 4 + q) * PER_SLOT + u;   // A loads first, then B
+                for (int n = 0; n < LOADS; ++n) {
+                    if (n * SLOTS / LOADS != s * 4 + q) continue;
                     if (n < P::A_LD) a_load(n, ka, sa_next);
                     else b_load(n - P::A_LD, kbo, sb_next);
                 }
@@ -228,12 +230,13 @@ __device__ __forceinline__ int pipe_out_row(int tid, int i, int r) {
     const int wm = (tid >> 6) & 1;
     return PipeTile::a_row(wm, i) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
-// SPLIT: column within a half (fragment j < 2); else column of the tile.
+// SPLIT: column within a half (the same for both fragments); else column of
+// the tile.
 template <bool SPLIT>
 __device__ __forceinline__ int pipe_out_col(int tid, int j) {
     const int lane = tid & 63;
     const int wn = (tid >> 6) >> 1;
-    return (SPLIT ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+    return SPLIT ? wn * 32 + (lane & 31) : wn * 64 + j * 32 + (lane & 31);
 }
 
 }  // namespace moe

@@ -246,7 +246,7 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
                                             const OperandRows &rows, int zc0, int zw,
                                             size_t rbase, int &k) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
-    pipe_gemm_nf<true, NF>(lds, rows, a.d, 0, 1, 0, acc);
+    pipe_gemm_nf<true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
     const int item = publish_item(lds, a, k);
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
     // split group the residual z - hi goes, rounded, zw columns further.
@@ -375,9 +375,10 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
                                          int my_pair, float my_gate, int &k) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
     if (tj.shared)
-        pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, acc);
+        pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs,
+                                split ? K / 2 : 0, acc);
     else
-        pipe_gemm_nf<false, NF>(lds, rows, K, split ? a.f : 0, 1, 0, acc);
+        pipe_gemm_nf<false, NF>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
     int2 *info = (int2 *)(lds + kRowInfoOffset);
     if (!tj.shared && threadIdx.x < PipeTile::BM)
         info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
@@ -424,7 +425,8 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
     const int goff = tj.shared ? 0 : a.group_off[tj.g];
-    // K runs over z, or over (hi, lo) of a split group, reusing W2
+    // K runs over z, or over (hi, lo) of a split group: the two halves of
+    // each 64-wide k-range back to back, so W2 streams once
     const int split = tj.shared ? a.split_s : a.split_r;
     const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;

@@ -114,7 +114,7 @@ __device__ __forceinline__ void load_lds16(const uint16_t *src, char *lds_dst) {
 // matrices side by side along K, possibly repeated).
 template <bool SPLIT, int NF>
 __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows, int K, int bsplit,
-                                             int bmod, size_t bstride,
+                                             int bmod, size_t bstride, int a_half,
                                              f32x16 (&acc)[NF > 0 ? NF : 1][PipeTile::FN]) {
     using P = PipeTile;
     const int tid = threadIdx.x;
@@ -136,9 +136,17 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
         return (bsplit > 0) ? (size_t)((k0 / bsplit) % bmod) * bstride + (size_t)(k0 % bsplit)
                             : (size_t)k0;
     };
+    // a_half > 0: A rows are two halves of a_half values (a bf16 (hi, lo)
+    // pair) and k-tile kt is half kt % 2 of k-range kt / 2; B's k-tile is
+    // k-range kt / 2 for both, so each B tile is loaded twice in a row (the
+    // second time from L2) instead of once per half pass.
+    auto a_col = [&](int kt) -> int {
+        return a_half ? (kt & 1) * a_half + (kt >> 1) * P::BK : kt * P::BK;
+    };
+    auto b_koff = [&](int kt) -> size_t { return koff_of((a_half ? kt >> 1 : kt) * P::BK); };
     auto a_load = [&](int n, int kt, int stage) {
         if ((rows.amask >> n) & 1)
-            load_lds16(rows.abase + rows.aoff[n] + kt * P::BK + ca,
+            load_lds16(rows.abase + rows.aoff[n] + a_col(kt) + ca,
                        a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
     };
     auto b_load = [&](int n, size_t koff, int stage) {
@@ -147,16 +155,17 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
     };
     const int nk = K / P::BK;
     // Prologue: A(0), B(0), B(1).  Every iteration kt then issues A(kt+1)
-    // followed by B(kt+2) (clamped to the last k-tile: trailing refetches
-    // land in a stage nobody reads any more).  So at the top of iteration kt
-    // the only loads issued after A(kt) and B(kt) are the B_LD loads of
-    // B(kt+1): vmcnt <= B_LD means both operands of k-tile kt have landed
-    // (vector memory loads complete in order).
+    // followed by B(kt+2), as far as they exist.  So at the top of iteration
+    // kt < nk-1 the only loads issued after A(kt) and B(kt) are the B_LD
+    // loads of B(kt+1): vmcnt <= B_LD means both operands of k-tile kt have
+    // landed (vector memory loads complete in order); the last iteration
+    // has nothing in flight after them and waits for everything.
 #pragma unroll
     for (int n = 0; n < P::A_LD; ++n) a_load(n, 0, 0);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        const size_t ko = koff_of(min(s, nk - 1) * P::BK);
+        if (s >= nk) break;
+        const size_t ko = b_koff(s);
 #pragma unroll
         for (int n = 0; n < P::B_LD; ++n) b_load(n, ko, s);
     }
@@ -164,10 +173,13 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
     constexpr int SLOTS = 4 * SUB;           // MFMA groups per k-tile
     constexpr int LOADS = P::A_LD + P::B_LD;
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<P::B_LD>();   // A(kt) and B(kt) have landed (this thread's share)
+        // A(kt) and B(kt) have landed (this thread's share) ...
+        if (kt + 1 < nk) wait_vmcnt<P::B_LD>();
+        else wait_vmcnt<0>();
         lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
+        const bool more_a = kt + 1 < nk, more_b = kt + 2 < nk;
         const int ka = min(kt + 1, nk - 1);
-        const size_t kbo = koff_of(min(kt + 2, nk - 1) * P::BK);
+        const size_t kbo = b_koff(min(kt + 2, nk - 1));
         const int sa_next = (kt + 1) % P::A_STAGES;
         const int sb_next = (kt + 2) % P::B_STAGES;
         const u32x4 *Ab = (const u32x4 *)(a_lds + (kt % P::A_STAGES) * P::A_STAGE);
@@ -203,14 +215,17 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
 #pragma unroll
                 for (int n = 0; n < LOADS; ++n) {
                     if (n * SLOTS / LOADS != s * 4 + q) continue;
-                    if (n < P::A_LD) a_load(n, ka, sa_next);
-                    else b_load(n - P::A_LD, kbo, sb_next);
+                    if (n < P::A_LD) {
+                        if (more_a) a_load(n, ka, sa_next);
+                    } else if (more_b) {
+                        b_load(n - P::A_LD, kbo, sb_next);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
-    wait_vmcnt<0>();   // trailing refetches land before the LDS is reused
+    wait_vmcnt<0>();
     lds_barrier();     // every wave done with the stages before the LDS is reused
 }
 

@@ -133,6 +133,38 @@ def test_skewed_and_empty_experts():
     caller_routing_case(cfg, idx, gate)
 
 
+def test_one_hot_expert_stealing_and_column_order():
+    """Every token on expert 7 and half of them also on expert 3: expert 7
+    spans 8 row tiles (listed column tile fastest), the other XCDs have no
+    work of their own and take items from the busy XCD's queue.  Repeated
+    calls are bitwise identical whatever the pull order."""
+    cfg = scaled(CONFIGS["v3_prefill"], T=2000, d_model=256, d_ff=128).with_(top_k=2)
+    idx = np.full((cfg.T, 2), -1, np.int32)
+    idx[:, 0] = 7
+    idx[::2, 1] = 3
+    gate = np.random.default_rng(3).random((cfg.T, 2)).astype(np.float32)
+    caller_routing_case(cfg, idx, gate)
+    inp = small_inputs(cfg)
+    i_t, w_t = torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda()
+    outs = [B.forward(cfg, inp.x, i_t, w_t, inp.w13, inp.w2, inp.w13s, inp.w2s) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+
+
+def test_many_experts_select_path():
+    """N' = 1024 routed experts (16 per lane in the select kernel), top-8."""
+    cfg = scaled(CONFIGS["v3_prefill"], T=300, d_model=256, d_ff=64).with_(
+        name="n1024", n_routed=1024)
+    inp = small_inputs(cfg)
+    r = gpu_layer(cfg, inp)
+    idx, gate = check_routing_identical_logits(cfg, inp, r)
+    tokens = np.arange(cfg.T)
+    _, _, _, gap = O.route(to_numpy(r["logits"]), cfg.n_routed, cfg.top_k, cfg.scoring,
+                           cfg.renorm, bias=host(inp.bias))
+    compare_h(cfg, gpu_h_as_f64(r["h"]), oracle_h(cfg, inp, tokens, idx, gate), gap)
+
+
 def test_segmentation_identity_on_gpu():
     """m fine experts (column slices) with the coarse gate reproduce the
     coarse expert: the GPU layer agrees with itself across the split."""

@@ -292,13 +292,23 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
     return item;
 }
 
+// Row tile m.  A group of cnt rows has R = ceil(cnt / bm) row tiles; its
+// rows are dealt out evenly in whole 32-row fragments: every tile but the
+// last holds rpt = 32 ceil(cnt / (32 R)) rows (rpt <= bm, and the last tile
+// is never empty).  The row tiles of one group then carry the same MFMA
+// work and run at the same speed, so the tiles that stream one weight tile
+// -- adjacent in the queue -- stay close enough for the later ones to find
+// it in L2 (EA read traffic of the V3 gate/up launch 32.0 -> 25.7 GB).
 __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm) {
     TileJob t;
     t.g = a.rtg[m];
     t.i = m - a.mt_base[t.g];
     t.j = 0;
-    t.row0 = t.i * bm;
-    t.nrows = min(bm, a.group_cnt[t.g] - t.row0);
+    const int cnt = a.group_cnt[t.g];
+    const int R = a.mt_base[t.g + 1] - a.mt_base[t.g];
+    const int rpt = min(bm, 32 * ((cnt + 32 * R - 1) / (32 * R)));
+    t.row0 = t.i * rpt;
+    t.nrows = min(rpt, cnt - t.row0);
     t.shared = (t.g == a.n_routed);
     return t;
 }

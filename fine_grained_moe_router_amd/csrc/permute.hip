@@ -105,18 +105,27 @@ __device__ int block_excl_scan(int32_t *data, int n, int32_t *tmp) {
     return total;
 }
 
+// Rows per row tile of a group of cnt rows in R tiles of at most bm rows:
+// the rows are dealt out evenly in 32-row fragments (the expert GEMMs'
+// row_tile); the last tile holds the rest.
+__device__ __forceinline__ int tile_rows(int cnt, int R, int bm) {
+    return min(bm, 32 * ((cnt + 32 * R - 1) / (32 * R)));
+}
+
 // Per-XCD row-tile ranges of one GEMM, balanced by estimated cost: a row
 // tile with r valid rows costs nt (2 + ceil(r / 64)) (nt column tiles, each
 // streaming its weight tile and issuing MFMAs for ceil(r / 64) 64-row
 // slices), with nt scaled by the group's relative K where it differs.  Row
-// tile m of group g starts at cost gcost_base[g] + i nt 6 (all but a
-// group's last row tile are full).  XCD x takes the row tiles whose
-// start cost lies in [x C / 8, (x + 1) C / 8).
-__device__ void xcd_splits(int G, const int32_t *cnt, const int32_t *mtb, const int32_t *ntg,
-                           int32_t *gcost, int32_t *tmp, int32_t *out) {
+// tile i of group g starts at cost gcost_base[g] + i nt (2 + ceil(rpt / 64))
+// (all but a group's last row tile hold rpt rows).  XCD x takes the row
+// tiles whose start cost lies in [x C / 8, (x + 1) C / 8).
+__device__ void xcd_splits(int G, int bm, const int32_t *cnt, const int32_t *mtb,
+                           const int32_t *ntg, int32_t *gcost, int32_t *tmp, int32_t *out) {
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
         const int mt = mtb[g + 1] - mtb[g];
-        gcost[g] = ntg[g] * (2 * mt + (cnt[g] + 63) / 64);
+        const int rpt = mt > 0 ? tile_rows(cnt[g], mt, bm) : 0;
+        const int last = cnt[g] - (mt - 1) * rpt;
+        gcost[g] = mt > 0 ? ntg[g] * (2 * mt + (mt - 1) * ((rpt + 63) / 64) + (last + 63) / 64) : 0;
     }
     __syncthreads();
     const int C = block_excl_scan(gcost, G, tmp);   // gcost now holds the group start costs
@@ -130,13 +139,16 @@ __device__ void xcd_splits(int G, const int32_t *cnt, const int32_t *mtb, const 
             if (mtb[mid] <= m) lo = mid;
             else hi = mid;
         }
-        const long long start = gcost[lo] + (long long)(m - mtb[lo]) * ntg[lo] * 6;
+        const int rpt = tile_rows(cnt[lo], mtb[lo + 1] - mtb[lo], bm);
+        const long long start =
+            gcost[lo] + (long long)(m - mtb[lo]) * ntg[lo] * (2 + (rpt + 63) / 64);
         long long prev = -1;
         if (m > 0) {
             const int pm = m - 1;
             int plo = (mtb[lo] <= pm) ? lo : lo - 1;
             while (plo > 0 && mtb[plo] > pm) --plo;
-            prev = gcost[plo] + (long long)(pm - mtb[plo]) * ntg[plo] * 6;
+            const int prpt = tile_rows(cnt[plo], mtb[plo + 1] - mtb[plo], bm);
+            prev = gcost[plo] + (long long)(pm - mtb[plo]) * ntg[plo] * (2 + (prpt + 63) / 64);
         }
         for (int x = 1; x < 8; ++x) {
             const long long target = (long long)x * C / 8;
@@ -220,8 +232,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
     for (int g = threadIdx.x; g <= G; g += blockDim.x) meta[mi.mt + g] = mtb[g];
     for (int g = threadIdx.x; g < G; g += blockDim.x)
         for (int m = mtb[g]; m < mtb[g + 1]; ++m) rtg[m] = g;
-    xcd_splits(G, cnt, mtb, nt1, gcost, tmp, meta + mi.xs1);
-    xcd_splits(G, cnt, mtb, nt2, gcost, tmp, meta + mi.xs2);
+    xcd_splits(G, ts.bm1, cnt, mtb, nt1, gcost, tmp, meta + mi.xs1);
+    xcd_splits(G, ts.bm1, cnt, mtb, nt2, gcost, tmp, meta + mi.xs2);
     // row offsets of the routed groups (the shared group reads rows 0..T-1)
     if (threadIdx.x == 0 && n_shared > 0) cnt[N] = 0;
     __syncthreads();

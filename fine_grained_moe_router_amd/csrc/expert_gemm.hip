@@ -85,21 +85,7 @@ __device__ __forceinline__ TileRange tile_range(int total) {
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-// Bit n set when A load n of this thread fetches one of the nrows valid rows.
-__device__ __forceinline__ uint32_t valid_row_mask(int nrows) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int n = 0; n < PipeTile::A_LD; ++n)
-        m |= (PipeTile::load_row(threadIdx.x, n) < nrows ? 1u : 0u) << n;
-    return m;
-}
 
-// Fragments (of 4) wave row wm must compute for a tile with nrows valid rows.
-__device__ __forceinline__ int wave_frags(int nrows) {
-    const int wm = (threadIdx.x >> 6) & 1;
-    const int nblk = (nrows + 31) >> 5;
-    return min(4, max(0, (nblk - wm + 1) >> 1));
-}
 
 // Work queue of the bf16 kernels.  XCD x owns the row tiles
 // [xsplit[x], xsplit[x+1]) (balanced by cost); its work items are the

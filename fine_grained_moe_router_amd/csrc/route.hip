@@ -12,53 +12,70 @@
 #include <math.h>
 
 #include "common.h"
-#include "mfma_tile.h"
+#include "mfma_pipe.h"
 #include "simt_tile.h"
 
 namespace moe {
 
 // ============================================================ router GEMM
 
-using RouterTile = MfmaTile<64, 64, 2, 2, false>;
-
-// Block (m, n, z) computes rows m*64.., logits n*64.. over k-tiles
-// [z*kps, (z+1)*kps) of d.  With one split it writes the logits; with more
-// it writes its partial sum to part[z] and k_router_reduce adds them.
-__global__ __launch_bounds__(RouterTile::NT) void k_router_bf16(int T, int d, int N, int kps,
-                                                                const uint16_t *__restrict__ x,
-                                                                const uint16_t *__restrict__ wg,
-                                                                float *__restrict__ out) {
-    __shared__ u32x4 As[2 * RouterTile::LDS_A];
-    __shared__ u32x4 Bs[2 * RouterTile::LDS_B];
-    const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-    const int k0 = blockIdx.z * kps * kBK;
-    const int K = min(d - k0, kps * kBK);
-    out += (size_t)blockIdx.z * T * N;
-    const uint16_t *arow[RouterTile::A_LD];
-    const uint16_t *brow[RouterTile::B_LD];
+// bf16: the 256 x 256 tile engine of the expert GEMMs (mfma_pipe.h).  Block
+// (m, n, z) computes tokens m*256.., logits n*256.. over k-tiles
+// [z*kps, (z+1)*kps) of d; a tile spans all 256 experts of a V3-sized
+// router, so x is read once.  With one split the block writes the logits;
+// with more it writes its partial sum to part[z] and k_router_reduce adds
+// them in split order.
+template <int NF>
+__device__ __forceinline__ void router_tile(char *lds, const OperandRows &rows, int K, int T,
+                                            int N, int m0, int n0, float *__restrict__ out) {
+    f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
+    pipe_gemm_nf<false, NF>(lds, rows, K, 0, 1, 0, 0, acc);
 #pragma unroll
-    for (int i = 0; i < RouterTile::A_LD; ++i) {
-        int r = m0 + RouterTile::load_row(threadIdx.x, i);
-        arow[i] = (r < T) ? x + (size_t)r * d + k0 : nullptr;
-    }
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
-    for (int i = 0; i < RouterTile::B_LD; ++i) {
-        int r = n0 + RouterTile::load_row(threadIdx.x, i);
-        brow[i] = (r < N) ? wg + (size_t)r * d + k0 : nullptr;
-    }
-    f32x16 acc[RouterTile::FM][RouterTile::FN];
-    RouterTile::run(arow, brow, K, 0, 1, 0, As, Bs, acc);
-#pragma unroll
-    for (int i = 0; i < RouterTile::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < RouterTile::FN; ++j) {
-            const int col = n0 + RouterTile::out_col(j);
+        for (int j = 0; j < PipeTile::FN; ++j) {
+            const int tid = opaque_tid();
+            const int col = n0 + pipe_out_col<false>(tid, j);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + RouterTile::out_row(i, r);
+                const int row = m0 + pipe_out_row(tid, i, r);
                 if (row < T && col < N) out[(size_t)row * N + col] = acc[i][j][r];
             }
         }
+}
+
+__global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int N, int kps,
+                                                              const uint16_t *__restrict__ x,
+                                                              const uint16_t *__restrict__ wg,
+                                                              float *__restrict__ out) {
+    __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
+    using P = PipeTile;
+    const int m0 = blockIdx.x * P::BM, n0 = blockIdx.y * P::BN;
+    const int k0 = blockIdx.z * kps * P::BK;
+    const int K = min(d - k0, kps * P::BK);
+    out += (size_t)blockIdx.z * T * N;
+    const int nrows = min(P::BM, T - m0);
+    OperandRows rows;
+    rows.abase = x + k0;
+    rows.bbase = wg + k0;
+#pragma unroll
+    for (int l = 0; l < P::A_LD; ++l) {
+        const int r = P::load_row(threadIdx.x, l);
+        rows.aoff[l] = (uint32_t)(m0 + (r < nrows ? r : 0)) * (uint32_t)d;   // rows past T: not fetched
+    }
+    rows.amask = valid_row_mask(nrows);
+#pragma unroll
+    for (int l = 0; l < P::B_LD; ++l) {
+        const int n = min(n0 + P::load_row(threadIdx.x, l), N - 1);   // experts past N': discarded
+        rows.boff[l] = (uint32_t)n * (uint32_t)d;
+    }
+    switch (wave_frags(nrows)) {
+        case 4: return router_tile<4>(lds, rows, K, T, N, m0, n0, out);
+        case 3: return router_tile<3>(lds, rows, K, T, N, m0, n0, out);
+        case 2: return router_tile<2>(lds, rows, K, T, N, m0, n0, out);
+        case 1: return router_tile<1>(lds, rows, K, T, N, m0, n0, out);
+        default: return router_tile<0>(lds, rows, K, T, N, m0, n0, out);
+    }
 }
 
 // logits = sum of the split partials, added in split order.
@@ -91,13 +108,14 @@ __global__ __launch_bounds__(256) void k_router_f32(int T, int d, int N, const f
         }
 }
 
-// K splits of the bf16 router GEMM: enough blocks to cover the CUs when the
-// batch is small (decode), each split at least 8 k-tiles long.
+// K splits of the bf16 router GEMM: enough blocks to cover the CUs (one
+// 256 x 256 tile per CU), each split at least 8 k-tiles long.
 int router_splits(const moe_config &c) {
     if (c.dtype != MOE_BF16) return 1;
-    const int tiles = ((c.T + 63) / 64) * ((c.n_routed + 63) / 64);
-    const int nk = c.d_model / kBK;
-    int z = min(min(16, nk / 8), (256 + tiles - 1) / tiles);
+    const int tiles = ((c.T + PipeTile::BM - 1) / PipeTile::BM) *
+                      ((c.n_routed + PipeTile::BN - 1) / PipeTile::BN);
+    const int nk = c.d_model / PipeTile::BK;
+    int z = min(min(16, nk / 8), (device_cu_count() + tiles - 1) / tiles);
     if (z <= 1) return 1;
     const int kps = (nk + z - 1) / z;
     return (nk + kps - 1) / kps;
@@ -107,10 +125,11 @@ hipError_t launch_router_logits(const moe_config &c, const void *x, const void *
                                 float *logits, float *part, hipStream_t s) {
     const int z = router_splits(c);
     if (c.dtype == MOE_BF16) {
-        const int nk = c.d_model / kBK;
+        const int nk = c.d_model / PipeTile::BK;
         const int kps = (nk + z - 1) / z;
-        dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64, z);
-        hipLaunchKernelGGL(k_router_bf16, grid, dim3(RouterTile::NT), 0, s, c.T, c.d_model,
+        dim3 grid((c.T + PipeTile::BM - 1) / PipeTile::BM,
+                  (c.n_routed + PipeTile::BN - 1) / PipeTile::BN, z);
+        hipLaunchKernelGGL(k_router_bf16, grid, dim3(PipeTile::NT), 0, s, c.T, c.d_model,
                            c.n_routed, kps, (const uint16_t *)x, (const uint16_t *)wg,
                            z > 1 ? part : logits);
         if (z > 1) {

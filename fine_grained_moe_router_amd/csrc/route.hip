@@ -207,17 +207,30 @@ __device__ __forceinline__ void wave_token_scores(int N, int scoring, const floa
 }
 
 // Wave-wide argmax of (v desc, index asc) over the lanes whose idx is not
-// 0x7fffffff; every lane receives the winner.
-__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, kWave);
-        const int oi = __shfl_xor(idx, o, kWave);
-        if (oi != 0x7fffffff && (idx == 0x7fffffff || ov > v || (ov == v && oi < idx))) {
-            v = ov;
-            idx = oi;
-        }
+// 0x7fffffff; every lane receives the winner.  (v, index) pairs are totally
+// ordered, so the winner does not depend on the order of the reduction.  It
+// runs on DPP lane moves, without the LDS crossbar: swaps within quads, then
+// within half rows and rows (mirrors), then row broadcasts that leave the
+// wave's winner in lane 63, which is read back into a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_dpp_step(float &v, int &idx) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
+        __float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0x7fffffff, idx, CTRL, ROW_MASK, 0xF, false);
+    if (oi != 0x7fffffff && (idx == 0x7fffffff || ov > v || (ov == v && oi < idx))) {
+        v = ov;
+        idx = oi;
     }
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
+    argmax_dpp_step<0xB1, 0xF>(v, idx);    // quad_perm [1,0,3,2]: lane ^ 1
+    argmax_dpp_step<0x4E, 0xF>(v, idx);    // quad_perm [2,3,0,1]: lane ^ 2
+    argmax_dpp_step<0x141, 0xF>(v, idx);   // row_half_mirror: the two quads of 8 lanes
+    argmax_dpp_step<0x140, 0xF>(v, idx);   // row_mirror: the two halves of a 16-lane row
+    argmax_dpp_step<0x142, 0xA>(v, idx);   // row_bcast:15 into rows 1, 3
+    argmax_dpp_step<0x143, 0xC>(v, idx);   // row_bcast:31 into rows 2, 3
+    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    idx = __builtin_amdgcn_readlane(idx, 63);
 }
 
 // One wavefront per token.  Lane `lane` owns experts lane + 64 j, j < J.

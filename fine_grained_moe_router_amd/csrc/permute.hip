@@ -158,9 +158,29 @@ __device__ void xcd_splits(int G, int bm, const int32_t *cnt, const int32_t *mtb
     __syncthreads();
 }
 
-// One block.  Turns chunk counts into chunk bases (relative to the expert),
-// computes group row counts/offsets, the tile prefix sums of both GEMMs, the
-// row-tile prefix sums and the per-XCD row-tile ranges.
+// Chunk bases: block e turns expert e's chunk counts into exclusive prefix
+// sums over the chunks (the row of each chunk's first pair of e, relative
+// to the expert) and leaves the expert's row count in group_cnt[e].  At most
+// 256 chunks (perm_chunk), one per thread.
+__global__ __launch_bounds__(256) void k_chunk_scan(int N, int n_chunks, int32_t *__restrict__ cc,
+                                                    int32_t *__restrict__ group_cnt) {
+    __shared__ int32_t v[256];
+    const int e = blockIdx.x, c = threadIdx.x;
+    const int x = (c < n_chunks) ? cc[(size_t)c * N + e] : 0;
+    v[c] = x;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {   // inclusive scan
+        const int y = (c >= o) ? v[c - o] : 0;
+        __syncthreads();
+        v[c] += y;
+        __syncthreads();
+    }
+    if (c < n_chunks) cc[(size_t)c * N + e] = v[c] - x;
+    if (c == 255) group_cnt[e] = v[255];
+}
+
+// One block.  Computes group row counts/offsets, the tile prefix sums of
+// both GEMMs, the row-tile prefix sums and the per-XCD row-tile ranges.
 __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, int n_shared,
                                                     int f, int fsum, int d, int split_r,
                                                     int split_s, TileShape ts,
@@ -177,33 +197,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, 
         t2[e] = 0;
     }
     __syncthreads();
-    {
-        // Expert e's chunk counts become chunk bases.  Q = 1024 / Np threads
-        // share an expert (Np = N rounded up to a power of two); thread q
-        // takes a contiguous run of chunks and starts from the sum of the
-        // runs before it.
-        int Np = 1;
-        while (Np < N) Np <<= 1;
-        const int Q = 1024 / Np;
-        const int e = threadIdx.x % Np, q = threadIdx.x / Np;
-        const int per = (n_chunks + Q - 1) / Q;
-        const int c0 = min(n_chunks, q * per), c1 = min(n_chunks, c0 + per);
-        int part = 0;
-        if (e < N)
-            for (int c = c0; c < c1; ++c) part += cc[(size_t)c * N + e];
-        tmp[threadIdx.x] = part;
-        __syncthreads();
-        if (e < N) {
-            int run = 0;
-            for (int qq = 0; qq < q; ++qq) run += tmp[qq * Np + e];
-            for (int c = c0; c < c1; ++c) {
-                const int v = cc[(size_t)c * N + e];
-                cc[(size_t)c * N + e] = run;
-                run += v;
-            }
-            if (q == Q - 1) cnt[e] = run;
-        }
-    }
+    // group row counts (the chunk scan left each routed expert's total)
+    for (int e = threadIdx.x; e < N; e += blockDim.x) cnt[e] = meta[mi.group_cnt + e];
     if (threadIdx.x == 0 && n_shared > 0) cnt[N] = T;
     __syncthreads();
     const int ntn2 = (d + ts.bn2 - 1) / ts.bn2;
@@ -283,6 +278,8 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_perm_hist, dim3(L.n_chunks), dim3(256), (size_t)N * 4, s, P, N, L.chunk,
                        idx, cc, meta + mi.bad);
+    hipLaunchKernelGGL(k_chunk_scan, dim3(N), dim3(256), 0, s, N, L.n_chunks, cc,
+                       meta + mi.group_cnt);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, L.n_chunks, c.T, c.n_shared,
                        c.d_ff, c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
                        z_split_shared(c) ? 1 : 0, tile_shape(c), cc, meta,

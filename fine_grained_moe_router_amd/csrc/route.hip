@@ -152,7 +152,7 @@ constexpr int kMaxTopK = 16;
 
 // One or two tokens per wavefront: the per-token top-K' rounds are a chain of
 // dependent cross-lane steps, so latency is hidden by many resident waves.
-int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 2 * kSelWaves : kSelWaves; }
+int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 4 * kSelWaves : kSelWaves; }
 
 int select_blocks(const moe_config &c) {
     const int tpb = select_tokens_per_block(c);

@@ -101,7 +101,10 @@ typedef struct {
 #define MOE_WS_SEQSTAT 3  /* scratch of moe_seq_balance_stats                   */
 
 /* Bytes of the requested buffer for this config; 0 if the config is invalid
- * or unsupported. */
+ * or unsupported.  MOE_WS_ROUTE also depends on the current device: the
+ * router GEMM splits d into as many ranges as it takes to cover the
+ * device's compute units, and the workspace holds one partial per range.
+ * Query it with the device current that the calls will run on. */
 size_t moe_workspace_bytes(const moe_config *cfg, int which);
 
 /*

@@ -50,12 +50,21 @@ KERNEL_OF_STAGE = {"gate_up": "k_gate_up_bf16", "down": "k_down_bf16"}
 GEMM_SOURCES = ("common.h", "mfma_pipe.h", "expert_gemm.hip", "permute.hip", "api.hip")
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and blank space: what decides the kernels
+    (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", name), "rb") as fh:
+        with open(os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", name), encoding="utf-8") as fh:
             h.update(name.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

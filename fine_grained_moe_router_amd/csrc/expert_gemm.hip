@@ -13,11 +13,13 @@
 // of width f act as one of width K_s f), so the down projection sums them
 // inside one K loop.
 //
-// Scheduling: persistent blocks.  Logical tiles are ordered (group, column
-// tile, row tile) with the row tile fastest, so the row tiles that share a
-// weight tile are adjacent.  The logical range is cut into 8 contiguous
-// pieces, one per XCD (block b runs on XCD b % 8), so adjacent tiles share
-// that XCD's L2.  Every block walks a bounded range and exits.
+// Scheduling: persistent blocks, one per CU.  The bf16 kernels pull
+// (row tile, column tile) items from per-XCD work queues (see "Work queue"
+// below).  The fp32 kernels (64-row tiles, SIMT) order their tiles (group,
+// row tile, column tile) with the column tile fastest, so the column tiles
+// that share token rows are adjacent; the range is cut into 8 contiguous
+// pieces, one per XCD (block b runs on XCD b % 8), and every block strides
+// through its XCD's piece.
 #include "common.h"
 #include "mfma_pipe.h"
 #include "simt_tile.h"
@@ -41,24 +43,15 @@ struct TileJob {
     bool shared;
 };
 
-#ifndef MOE_TILE_ORDER
-#define MOE_TILE_ORDER 1
-#endif
-
 __device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, int bm) {
     TileJob t;
     t.g = find_group(a.tile_base, a.G, tile);
     const int rel = tile - a.tile_base[t.g];
     const int cnt = a.group_cnt[t.g];
     const int mt = (cnt + bm - 1) / bm;
-#if MOE_TILE_ORDER == 0
-    t.j = rel / mt;               // row tile fastest: row tiles sharing a weight tile adjacent
-    t.i = rel - t.j * mt;
-#else
     const int nt = (a.tile_base[t.g + 1] - a.tile_base[t.g]) / mt;
     t.i = rel / nt;               // column tile fastest: column tiles sharing rows adjacent
     t.j = rel - t.i * nt;
-#endif
     t.row0 = t.i * bm;
     t.nrows = min(bm, cnt - t.row0);
     t.shared = (t.g == a.n_routed);

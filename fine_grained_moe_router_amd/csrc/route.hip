@@ -240,9 +240,11 @@ __device__ __forceinline__ void wave_argmax(float &v, int &idx) {
 // Node-limited routing (n_groups > 0): the experts of the topk_groups groups
 // with the largest best key are the only candidates; the others are marked
 // taken before the top-K' rounds.
-template <int J>
+// SC: the scoring function (MOE_SCORE_*), a template argument so that only
+// its fp64 path is compiled into each instance.
+template <int J, int SC>
 __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
-    int T, int N, int K, int scoring, int renorm, int tpb, int n_groups, int topk_groups,
+    int T, int N, int K, int renorm, int tpb, int n_groups, int topk_groups,
     const float *__restrict__ logits, const float *__restrict__ offset,
     const float *__restrict__ bias, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
     int32_t *__restrict__ counts, double *__restrict__ p_partial) {
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
     const int t1 = min(T, t0 + tpb);
     for (int t = t0 + wave; t < t1; t += kSelWaves) {
         float l[J], key[J], s32[J];
-        wave_token_scores<J>(N, scoring, logits + (size_t)t * N, offset, lane, l, s32);
+        wave_token_scores<J>(N, SC, logits + (size_t)t * N, offset, lane, l, s32);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int e = lane + 64 * j;
@@ -367,16 +369,23 @@ hipError_t launch_select(const moe_config &c, const float *logits, const float *
     const int J = (c.n_routed + 63) / 64;
     const int tpb = select_tokens_per_block(c);
     dim3 grid(select_blocks(c)), block(kSelWaves * kWave);
-#define MOE_SEL(JJ)                                                                            \
-    hipLaunchKernelGGL(k_select<JJ>, grid, block, 0, s, c.T, c.n_routed, c.top_k, c.scoring,   \
+#define MOE_SEL_SC(JJ, SC)                                                                     \
+    hipLaunchKernelGGL((k_select<JJ, SC>), grid, block, 0, s, c.T, c.n_routed, c.top_k,       \
                        c.renorm, tpb, c.n_groups, c.topk_groups, logits, offset, bias, idx, w, \
                        counts, p_partial)
+#define MOE_SEL(JJ)                                                                            \
+    do {                                                                                       \
+        if (c.scoring == MOE_SCORE_SOFTMAX) MOE_SEL_SC(JJ, MOE_SCORE_SOFTMAX);                 \
+        else if (c.scoring == MOE_SCORE_SIGMOID) MOE_SEL_SC(JJ, MOE_SCORE_SIGMOID);            \
+        else MOE_SEL_SC(JJ, MOE_SCORE_SQRT_SOFTPLUS);                                          \
+    } while (0)
     if (J <= 1) MOE_SEL(1);
     else if (J <= 2) MOE_SEL(2);
     else if (J <= 4) MOE_SEL(4);
     else if (J <= 6) MOE_SEL(6);
     else if (J <= 8) MOE_SEL(8);
     else MOE_SEL(16);
+#undef MOE_SEL_SC
 #undef MOE_SEL
     return hipGetLastError();
 }

@@ -97,6 +97,9 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a calibration copy plus a few steps")
     ap.add_argument("--pmc-summary", default=None)
+    ap.add_argument("--clock-summary", default=None,
+                    help="directory of a rocprofv3 --pmc GRBM_GUI_ACTIVE run of the layer step: "
+                         "write the effective clock of its long kernels to profiles/")
     ap.add_argument("--extras", action="store_true",
                     help="time the entry points beyond the layer step (node-limited routing, "
                          "in-sequence and device-level statistics, bias update) instead")
@@ -231,6 +234,44 @@ def pmc_summary(out_dir: str, workload: str, stage: str = "gate_up"):
     print(json.dumps({"traffic_bytes_per_launch": traffic, "record": traffic_record_path(workload, stage)}))
 
 
+def clock_summary(out_dir: str, workload: str, min_ms: float = 0.5):
+    """Effective clock of the kernels of a rocprofv3 --pmc GRBM_GUI_ACTIVE run:
+    GPU-active cycles (summed over the XCDs, so divided by their count) over
+    the dispatch's duration.  Only dispatches of at least min_ms count: the
+    counter window is wider than the kernel, which inflates short ones."""
+    rows, n_xcc = [], None
+    for p in glob.glob(os.path.join(out_dir, "**", "*agent_info.csv"), recursive=True):
+        with open(p) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Agent_Type") == "GPU" and r.get("Num_Xcc"):
+                    n_xcc = int(r["Num_Xcc"])
+    for p in glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as fh:
+            rows += [r for r in csv.DictReader(fh) if r.get("Counter_Name") == "GRBM_GUI_ACTIVE"]
+    if not rows or not n_xcc:
+        raise SystemExit(f"no GRBM_GUI_ACTIVE rows or GPU agent under {out_dir}")
+    by = {}
+    for r in rows:
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if ns >= min_ms * 1e6:
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            by.setdefault(name, []).append((float(r["Counter_Value"]) / n_xcc / ns, ns / 1e6))
+    out = {}
+    for name, v in sorted(by.items()):
+        ghz = sorted(g for g, _ in v)
+        out[name] = {"dispatches": len(v), "ghz_median": round(ghz[len(ghz) // 2], 3),
+                     "ghz_min": round(ghz[0], 3), "ghz_max": round(ghz[-1], 3),
+                     "ms_median": round(sorted(m for _, m in v)[len(v) // 2], 3)}
+    rec = {"workload": workload, "xcds": n_xcc, "kernels": out,
+           "commands": [f"rocprofv3 --pmc GRBM_GUI_ACTIVE -d {out_dir} -o run --output-format csv -- "
+                        f"python3 bench.py --workload {workload} --no-cpu-baseline",
+                        f"python3 bench.py --clock-summary {out_dir} --workload {workload}"]}
+    path = os.path.join(ROOT, "profiles", f"clock_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({"record": path, "kernels": out}))
+
+
 def time_calls(fn, reps=50):
     """Average ms of fn() over reps calls, HIP events on torch's current
     stream (the binding launches on that stream)."""
@@ -321,6 +362,9 @@ def main(argv=None):
         return 2
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.workload)
+        return 0
+    if args.clock_summary:
+        clock_summary(args.clock_summary, args.workload)
         return 0
 
     import torch

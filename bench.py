@@ -234,7 +234,7 @@ def pmc_summary(out_dir: str, workload: str, stage: str = "gate_up"):
     print(json.dumps({"traffic_bytes_per_launch": traffic, "record": traffic_record_path(workload, stage)}))
 
 
-def clock_summary(out_dir: str, workload: str, min_ms: float = 0.5):
+def clock_summary(out_dir: str, workload: str, min_ms: float = 0.5, path: str | None = None):
     """Effective clock of the kernels of a rocprofv3 --pmc GRBM_GUI_ACTIVE run:
     GPU-active cycles (summed over the XCDs, so divided by their count) over
     the dispatch's duration.  Only dispatches of at least min_ms count: the
@@ -266,7 +266,7 @@ def clock_summary(out_dir: str, workload: str, min_ms: float = 0.5):
            "commands": [f"rocprofv3 --pmc GRBM_GUI_ACTIVE -d {out_dir} -o run --output-format csv -- "
                         f"python3 bench.py --workload {workload} --no-cpu-baseline",
                         f"python3 bench.py --clock-summary {out_dir} --workload {workload}"]}
-    path = os.path.join(ROOT, "profiles", f"clock_{workload}.json")
+    path = path or os.path.join(ROOT, "profiles", f"clock_{workload}.json")
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps({"record": path, "kernels": out}))

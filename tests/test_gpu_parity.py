@@ -218,7 +218,7 @@ def test_full_size_workload(name):
     if cfg.T <= 64:
         tokens = np.arange(cfg.T)
     else:
-        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 10, replace=False)]))
+        tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 38, replace=False)]))
     print(f"[full-size] {name}: oracle on {len(tokens)} tokens", flush=True)
     x_h = host(inp.x)
     _, idx, gate, _, gap = oracle_route_tokens(cfg, inp, tokens, x_h=x_h)

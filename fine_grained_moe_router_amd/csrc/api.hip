@@ -195,6 +195,8 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     a.zs = ws + L.off_zs;
     a.yr = (float *)(ws + L.off_yr);
     a.ys = (float *)(ws + L.off_ys);
+    a.yrh = (uint16_t *)(ws + L.off_yrh);
+    a.ysh = (uint16_t *)(ws + L.off_ysh);
     {
         StageScope sc(MOE_STAGE_GATE_UP, s);
         a.tile_base = meta + mi.tile1;
@@ -211,7 +213,7 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     }
     {
         StageScope sc(MOE_STAGE_COMBINE, s);
-        if ((e = launch_combine(c, x, topk_idx, a.yr, a.ys, h, s)) != hipSuccess) return hip_fail(e);
+        if ((e = launch_combine(c, x, topk_idx, a.yr, a.ys, a.yrh, a.ysh, h, s)) != hipSuccess) return hip_fail(e);
     }
     return MOE_OK;
 }

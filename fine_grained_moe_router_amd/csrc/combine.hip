@@ -2,9 +2,10 @@
 // of the DeepSeekMoE notes):
 //   h_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx[t][k]}(u_t)
 // The gate-scaled routed outputs arrive in pair order (t K' + k), the summed
-// shared output per token.  Each thread adds four columns in a fixed order
-// (residual, shared, then k = 0..K'-1) in fp32 and rounds once, so the
-// result is the same bit pattern on every run (no atomics).
+// shared output per token: fp32 for fp32 layers, fp16 for bf16 layers (with
+// fp32 kept where fp16 overflows; f16x4_load).  Each thread adds four columns
+// in a fixed order (residual, shared, then k = 0..K'-1) in fp32 and rounds
+// once, so the result is the same bit pattern on every run (no atomics).
 #include "common.h"
 
 namespace moe {
@@ -14,7 +15,10 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
                                                  const void *__restrict__ x,
                                                  const int32_t *__restrict__ idx,
                                                  const float *__restrict__ yr,
-                                                 const float *__restrict__ ys, void *__restrict__ h) {
+                                                 const float *__restrict__ ys,
+                                                 const uint16_t *__restrict__ yrh,
+                                                 const uint16_t *__restrict__ ysh,
+                                                 void *__restrict__ h) {
     const int ncb = (d / 4 + blockDim.x - 1) / blockDim.x;
     const int t = blockIdx.x / ncb;
     const int c = ((blockIdx.x % ncb) * blockDim.x + threadIdx.x) * 4;
@@ -31,7 +35,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
         acc = *(const float4 *)((const float *)x + o);
     }
     if (has_shared) {
-        const float4 s = *(const float4 *)(ys + o);
+        const float4 s = BF16 ? f16x4_load(ysh + o, ys + o) : *(const float4 *)(ys + o);
         acc.x += s.x;
         acc.y += s.y;
         acc.z += s.z;
@@ -40,7 +44,8 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
     for (int k = 0; k < K; ++k) {
         const int e = idx[(size_t)t * K + k];
         if (e < 0 || e >= N) continue;
-        const float4 y = *(const float4 *)(yr + ((size_t)t * K + k) * d + c);
+        const size_t oy = ((size_t)t * K + k) * d + c;
+        const float4 y = BF16 ? f16x4_load(yrh + oy, yr + oy) : *(const float4 *)(yr + oy);
         acc.x += y.x;
         acc.y += y.y;
         acc.z += y.z;
@@ -57,14 +62,15 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
 }
 
 hipError_t launch_combine(const moe_config &c, const void *x, const int32_t *idx, const float *yr,
-                          const float *ys, void *h, hipStream_t s) {
+                          const float *ys, const uint16_t *yrh, const uint16_t *ysh, void *h,
+                          hipStream_t s) {
     dim3 grid(((c.d_model / 4 + 255) / 256) * c.T);
     if (c.dtype == MOE_BF16)
         hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, c.T, c.d_model, c.top_k,
-                           c.n_routed, c.n_shared > 0, x, idx, yr, ys, h);
+                           c.n_routed, c.n_shared > 0, x, idx, yr, ys, yrh, ysh, h);
     else
         hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, c.T, c.d_model, c.top_k,
-                           c.n_routed, c.n_shared > 0, x, idx, yr, ys, h);
+                           c.n_routed, c.n_shared > 0, x, idx, yr, ys, yrh, ysh, h);
     return hipGetLastError();
 }
 

@@ -30,6 +30,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// ---- fp16 staging of the expert outputs (bf16 layers) ----------------------
+// The gate-scaled expert outputs travel from the down projection to the
+// combine as fp16: 11 significant bits against bf16's 8, at half the bytes of
+// fp32.  A group of four values is stored as four halves.  When one of them
+// has no finite fp16 form (|v| >= 65520 rounds to infinity; NaN stays NaN),
+// its all-ones exponent marks the group, which is then also stored as fp32 at
+// the same index of an fp32 array, and the reader takes it from there.  So
+// the combine sees every value either as fp16(v) or as v itself.
+__device__ __forceinline__ uint32_t f16x2_pack(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+}
+__device__ __forceinline__ bool f16x4_marked(uint2 p) {
+    return ((p.x & 0x7C00u) == 0x7C00u) | ((p.x & 0x7C000000u) == 0x7C000000u) |
+           ((p.y & 0x7C00u) == 0x7C00u) | ((p.y & 0x7C000000u) == 0x7C000000u);
+}
+__device__ __forceinline__ void f16x4_store(uint16_t *h, float *f, float4 v) {
+    const uint2 p = make_uint2(f16x2_pack(v.x, v.y), f16x2_pack(v.z, v.w));
+    *(uint2 *)h = p;
+    if (f16x4_marked(p)) *(float4 *)f = v;
+}
+__device__ __forceinline__ float4 f16x4_load(const uint16_t *h, const float *f) {
+    const uint2 p = *(const uint2 *)h;
+    if (f16x4_marked(p)) return *(const float4 *)f;
+    return make_float4(f16_lo(p.x), f16_hi(p.x), f16_lo(p.y), f16_hi(p.y));
+}
+
 // ---- wave reductions (64 lanes) --------------------------------------------
 __device__ __forceinline__ double wave_sum_f64(double v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -58,6 +91,8 @@ struct FwdLayout {
     size_t off_zs;      // [T][K_s*d_ff_shared] dtype: shared hidden activations
     size_t off_yr;      // fp32 [T*K'][d]: gate-scaled routed outputs, pair order
     size_t off_ys;      // fp32 [T][d]: summed shared-expert outputs
+    size_t off_yrh;     // bf16 layers: fp16 copies of the two above, read by
+    size_t off_ysh;     //   the combine (fp32 only where fp16 overflows)
     size_t total;
 };
 
@@ -110,6 +145,7 @@ struct GroupedArgs {
     const void *x, *w13, *w2, *w13s, *w2s;
     void *zr, *zs;
     float *yr, *ys;
+    uint16_t *yrh, *ysh;      // fp16 outputs of the bf16 kernels (see f16x4_store)
 };
 
 // ---- launchers (each returns hipSuccess or the launch error) ---------------
@@ -151,7 +187,8 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
 hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a, hipStream_t s);
 hipError_t launch_down(const moe_config &c, const GroupedArgs &a, hipStream_t s);
 hipError_t launch_combine(const moe_config &c, const void *x, const int32_t *idx,
-                          const float *yr, const float *ys, void *h, hipStream_t s);
+                          const float *yr, const float *ys, const uint16_t *yrh,
+                          const uint16_t *ysh, void *h, hipStream_t s);
 
 int device_cu_count();
 

@@ -373,24 +373,29 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
         info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
     const int item = publish_item(lds, a, k);   // its barrier also publishes info
     // Four rows of one column are transposed across a lane quad: each lane
-    // then stores four consecutive fp32 columns of one row (16 bytes).
+    // then stores four consecutive columns of one row, as fp16 (8 bytes; the
+    // fp32 array only where fp16 overflows, see f16x4_store).
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
             const int tid = opaque_tid();
             const int row = quad_row(tid, i, rq);
-            float *dst = nullptr;
+            size_t o = 0;
+            bool live = false, shared = tj.shared;
             float gate = 1.0f;
             if (row < tj.nrows) {
-                if (tj.shared) {
-                    dst = a.ys + (size_t)(tj.row0 + row) * a.d;
+                live = true;
+                if (shared) {
+                    o = (size_t)(tj.row0 + row) * a.d;
                 } else {
                     const int2 v = info[row];
                     gate = __int_as_float(v.y);
-                    dst = a.yr + (size_t)v.x * a.d;
+                    o = (size_t)v.x * a.d;
                 }
             }
+            float *dst = shared ? a.ys + o : a.yr + o;
+            uint16_t *dsth = shared ? a.ysh + o : a.yrh + o;
 #pragma unroll
             for (int j = 0; j < PipeTile::FN; ++j) {
                 float v[4];
@@ -398,9 +403,9 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
                 for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * rq + q];
                 quad_transpose(v, tid & 3);
                 const int col = n0 + (pipe_out_col<false>(tid, j) & ~3);
-                if (dst && col < a.d)
-                    *(float4 *)(dst + col) = make_float4(gate * v[0], gate * v[1], gate * v[2],
-                                                         gate * v[3]);
+                if (live && col < a.d)
+                    f16x4_store(dsth + col, dst + col,
+                                make_float4(gate * v[0], gate * v[1], gate * v[2], gate * v[3]));
             }
             __builtin_amdgcn_sched_barrier(0);
         }

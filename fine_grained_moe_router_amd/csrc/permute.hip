@@ -57,6 +57,11 @@ FwdLayout fwd_layout(const moe_config &c) {
     o = align256(o + P * c.d_model * 4);
     L.off_ys = o;
     o = align256(o + (size_t)(c.n_shared > 0 ? c.T : 0) * c.d_model * 4);
+    const size_t hb = c.dtype == MOE_BF16 ? 2 : 0;   // fp16 staging, bf16 layers only
+    L.off_yrh = o;
+    o = align256(o + P * c.d_model * hb);
+    L.off_ysh = o;
+    o = align256(o + (size_t)(c.n_shared > 0 ? c.T : 0) * c.d_model * hb);
     L.total = o;
     return L;
 }

@@ -165,8 +165,11 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_gate,
  * [0, N') contributes nothing.  Each selected (token, expert) pair is
  * computed once (dropless).  The result is bitwise reproducible run to run.
  * Arithmetic: bf16 products with fp32 accumulation; the SwiGLU hidden
- * activation is rounded once to the input dtype before the down projection;
- * the sum is formed in fp32 and rounded once (nearest-even) into h.
+ * activation is rounded to the input dtype before the down projection (for
+ * gate-1 groups with bf16, to a pair of bf16 values); with bf16, each
+ * gate-scaled expert output is held as fp16 until the sum (as fp32 where it
+ * exceeds fp16's range); the sum is formed in fp32 and rounded once
+ * (nearest-even) into h.
  * Arguments
  *   x          [T][d] (cfg->dtype)
  *   topk_idx   [T][K'] int32, topk_w [T][K'] fp32

@@ -133,6 +133,29 @@ def test_skewed_and_empty_experts():
     caller_routing_case(cfg, idx, gate)
 
 
+def test_outputs_beyond_fp16_range():
+    """bf16 layers stage the gate-scaled expert outputs as fp16 and keep fp32
+    where fp16 overflows.  W2 and the shared W2 scaled by 2^16 (exact in bf16,
+    so every expert output scales exactly): about a tenth of the outputs now
+    exceed fp16's range, the rest do not.  h must equal x + 2^16 Y to the
+    usual error of Y (scaled) plus h's own bf16 rounding."""
+    cfg = scaled(CONFIGS["v3_prefill"], T=300, d_model=256, d_ff=128)
+    inp = small_inputs(cfg)
+    scale = 2.0 ** 16
+    inp.w2 = (inp.w2.float() * scale).to(torch.bfloat16)
+    inp.w2s = (inp.w2s.float() * scale).to(torch.bfloat16)
+    r = gpu_layer(cfg, inp)
+    idx, gate = check_routing_identical_logits(cfg, inp, r)
+    tokens = np.arange(cfg.T)
+    h_ref = oracle_h(cfg, inp, tokens, idx, gate)
+    h_gpu = gpu_h_as_f64(r["h"])
+    assert np.isfinite(h_gpu).all()
+    assert (np.abs(h_ref) > 65520).mean() > 0.02          # the fp32 path is exercised
+    err = np.abs(h_gpu - h_ref)
+    assert (err <= scale * 6e-3 + 2.0 ** -8 * np.abs(h_ref)).all(), err.max()
+    assert np.linalg.norm(h_gpu - h_ref) <= 5e-3 * np.linalg.norm(h_ref)
+
+
 def test_one_hot_expert_stealing_and_column_order():
     """Every token on expert 7 and half of them also on expert 3: expert 7
     spans 8 row tiles (listed column tile fastest), the other XCDs have no

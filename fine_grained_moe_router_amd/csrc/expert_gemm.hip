@@ -151,7 +151,6 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
 // tile first writes it after the top barrier of its first k-tile, which
 // every wave reaches only after it has read the word.
 constexpr int kItemBits = 24;
-constexpr int kQueueSlotOffset = PipeTile::A_STAGE;
 static_assert(PipeTile::A_STAGES == 2, "queue slot lives in the second A stage");
 
 __device__ __forceinline__ int next_item(const GroupedArgs &a, int &k) {
@@ -166,8 +165,9 @@ __device__ __forceinline__ int next_item(const GroupedArgs &a, int &k) {
 }
 // Called by every thread right after the K loop of a tile (and once before
 // the first tile).
+template <class P>
 __device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int &k) {
-    int32_t *slot = (int32_t *)(lds + kQueueSlotOffset);
+    int32_t *slot = (int32_t *)(lds + P::A_STAGE);
     if (threadIdx.x == 0) *slot = next_item(a, k);
     lds_barrier();
     return __builtin_amdgcn_readfirstlane(*slot);
@@ -205,12 +205,11 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int p) {
 // Epilogue coordinates after quad_transpose of accumulator registers
 // 4 rq .. 4 rq + 3 of fragment i: the lane's output row, and the first of
 // its four consecutive columns relative to the fragment's column block.
+template <class P>
 __device__ __forceinline__ int quad_row(int tid, int i, int rq) {
     const int lane = tid & 63;
-    const int wm = (tid >> 6) & 1;
-    return PipeTile::a_row(wm, i) + rq * 8 + (lane >> 5) * 4 + (lane & 3);
+    return P::a_row(P::wave_m(tid), i) + rq * 8 + (lane >> 5) * 4 + (lane & 3);
 }
-__device__ __forceinline__ int quad_col(int tid) { return (tid & 31) & ~3; }
 
 __device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
     uint2 o;
@@ -220,13 +219,13 @@ __device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
 }
 
 // One gate/up tile whose wave computes NF row fragments.
-template <int NF>
+template <class P, int NF>
 __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                            const OperandRows &rows, int zc0, int zw,
+                                            const OperandRows<P> &rows, int zc0, int zw,
                                             size_t rbase, int &k) {
-    f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
-    pipe_gemm_nf<true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
-    const int item = publish_item(lds, a, k);
+    f32x16 acc[NF > 0 ? NF : 1][P::FN];
+    pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
+    const int item = publish_item<P>(lds, a, k);
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
     // split group the residual z - hi goes, rounded, zw columns further.
     // Four rows' z of one column are transposed across a lane quad so each
@@ -236,20 +235,21 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
     const size_t zstride = (size_t)zw * (split ? 2 : 1);
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-        {
+#pragma unroll
+        for (int jp = 0; jp < P::FN / 2; ++jp) {
             const int tid = opaque_tid();
-            const int col = zc0 + (pipe_out_col<true>(tid, 0) & ~3);
+            const int col = zc0 + (pipe_out_col<P, true>(tid, jp) & ~3);
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 float z[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float ga = acc[i][0][4 * rq + q];   // W1 (gate) fragment
-                    const float up = acc[i][1][4 * rq + q];   // W3 (up) fragment
+                    const float ga = acc[i][jp][4 * rq + q];              // W1 (gate) fragment
+                    const float up = acc[i][jp + P::FN / 2][4 * rq + q];  // W3 (up) fragment
                     z[q] = ga / (1.0f + __expf(-ga)) * up;
                 }
                 quad_transpose(z, tid & 3);
-                const int row = quad_row(tid, i, rq);
+                const int row = quad_row<P>(tid, i, rq);
                 if (row < tj.nrows && col < zw) {
                     uint16_t *dst = zout + (rbase + row) * zstride + col;
                     const uint2 hi = pack_bf16x4(z);
@@ -292,14 +292,14 @@ __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm)
     return t;
 }
 
+template <class P>
 __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob &tj, char *lds,
                                             int &k) {
-    using P = PipeTile;
     const int fsum = a.n_shared * a.fs;
     const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
     const int zc0 = tj.j * (P::BN / 2);            // first hidden column of the tile
     const int goff = tj.shared ? 0 : a.group_off[tj.g];
-    OperandRows rows;
+    OperandRows<P> rows;
     rows.abase = (const uint16_t *)a.x;
 #pragma unroll
     for (int l = 0; l < P::A_LD; ++l) {
@@ -308,7 +308,7 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
         const int tok = tj.shared ? tj.row0 + r : a.perm[goff + tj.row0 + r] / a.top_k;
         rows.aoff[l] = (uint32_t)tok * (uint32_t)a.d;
     }
-    rows.amask = valid_row_mask(tj.nrows);
+    rows.amask = valid_row_mask<P>(tj.nrows);
     // B rows: hidden columns zc0 .. zc0+127 of W1 (tile rows 0..127) and of
     // W3 (tile rows 128..255); the shared group's hidden columns run across
     // its K_s experts.
@@ -325,53 +325,57 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
         rows.boff[l] = ((uint32_t)js * 2 * wwidth + (up ? wwidth : 0) + c) * (uint32_t)a.d;
     }
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
-    switch (wave_frags(tj.nrows)) {
-        case 4: return gate_up_tile<4>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 3: return gate_up_tile<3>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 2: return gate_up_tile<2>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 1: return gate_up_tile<1>(a, tj, lds, rows, zc0, zw, rbase, k);
-        default: return gate_up_tile<0>(a, tj, lds, rows, zc0, zw, rbase, k);
+    switch (wave_frags<P>(tj.nrows)) {
+        case 4: return gate_up_tile<P, 4>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 3: return gate_up_tile<P, 3>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 2: return gate_up_tile<P, 2>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 1: return gate_up_tile<P, 1>(a, tj, lds, rows, zc0, zw, rbase, k);
+        default: return gate_up_tile<P, 0>(a, tj, lds, rows, zc0, zw, rbase, k);
     }
 }
 
-__global__ __launch_bounds__(PipeTile::NT) void k_gate_up_bf16(const GroupedArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
+template <class P>
+__global__ __launch_bounds__(P::NT) void k_gate_up_bf16(const GroupedArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
     int k = 0;
-    int item = publish_item(lds, a, k);
+    int item = publish_item<P>(lds, a, k);
     while (item >= 0) {
         int m, j;
         item_tile(a, item, m, j);
-        TileJob tj = row_tile(a, m, PipeTile::BM);
+        TileJob tj = row_tile(a, m, P::BM);
         tj.j = j;
-        item = gate_up_body(a, tj, lds, k);
+        item = gate_up_body<P>(a, tj, lds, k);
     }
 }
 
-// One down-projection tile whose wave computes NF row fragments.
-// (pair, gate) of row t of a routed tile sits in LDS word pair t of the
-// epilogue area: the third B stage, which no wave reads after the K loop and
-// which the next tile first writes after the top barrier of its first k-tile.
-constexpr int kRowInfoOffset = PipeTile::A_STAGES * PipeTile::A_STAGE + 2 * PipeTile::B_STAGE;
-static_assert(PipeTile::NT >= PipeTile::BM, "one tile row per thread");
-static_assert(PipeTile::B_STAGES == 3, "row info lives in the third B stage");
+// (pair, gate) of row t of a routed down tile sits in LDS word pair t of
+// the last B stage, which no wave reads after the K loop and which the next
+// tile first writes after the top barrier of its first k-tile (its prologue
+// fills the B stages before the last).
+template <class P>
+constexpr int row_info_offset() {
+    static_assert(P::NT >= P::BM, "one tile row per thread");
+    static_assert(P::BM * 8 <= P::B_STAGE, "row info fits one B stage");
+    return P::A_STAGES * P::A_STAGE + (P::B_STAGES - 1) * P::B_STAGE;
+}
 
 // One down-projection tile whose wave computes NF row fragments.  Thread t
 // brings the pair id and gate of tile row t (fetched before the K loop); the
 // epilogue reads them back from LDS, so its stores never wait on a load.
-template <int NF>
+template <class P, int NF>
 __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                         const OperandRows &rows, int K, int split, int n0,
+                                         const OperandRows<P> &rows, int K, int split, int n0,
                                          int my_pair, float my_gate, int &k) {
-    f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
+    f32x16 acc[NF > 0 ? NF : 1][P::FN];
     if (tj.shared)
-        pipe_gemm_nf<false, NF>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs,
-                                split ? K / 2 : 0, acc);
+        pipe_gemm_nf<P, false, NF, true>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs,
+                                         split ? K / 2 : 0, acc);
     else
-        pipe_gemm_nf<false, NF>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
-    int2 *info = (int2 *)(lds + kRowInfoOffset);
-    if (!tj.shared && threadIdx.x < PipeTile::BM)
+        pipe_gemm_nf<P, false, NF, true>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
+    int2 *info = (int2 *)(lds + row_info_offset<P>());
+    if (!tj.shared && threadIdx.x < P::BM)
         info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
-    const int item = publish_item(lds, a, k);   // its barrier also publishes info
+    const int item = publish_item<P>(lds, a, k);   // its barrier also publishes info
     // Four rows of one column are transposed across a lane quad: each lane
     // then stores four consecutive columns of one row, as fp16 (8 bytes; the
     // fp32 array only where fp16 overflows, see f16x4_store).
@@ -380,7 +384,7 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
             const int tid = opaque_tid();
-            const int row = quad_row(tid, i, rq);
+            const int row = quad_row<P>(tid, i, rq);
             size_t o = 0;
             bool live = false, shared = tj.shared;
             float gate = 1.0f;
@@ -397,12 +401,12 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
             float *dst = shared ? a.ys + o : a.yr + o;
             uint16_t *dsth = shared ? a.ysh + o : a.yrh + o;
 #pragma unroll
-            for (int j = 0; j < PipeTile::FN; ++j) {
+            for (int j = 0; j < P::FN; ++j) {
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * rq + q];
                 quad_transpose(v, tid & 3);
-                const int col = n0 + (pipe_out_col<false>(tid, j) & ~3);
+                const int col = n0 + (pipe_out_col<P, false>(tid, j) & ~3);
                 if (live && col < a.d)
                     f16x4_store(dsth + col, dst + col,
                                 make_float4(gate * v[0], gate * v[1], gate * v[2], gate * v[3]));
@@ -413,9 +417,9 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     return item;
 }
 
+template <class P>
 __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj, char *lds,
                                          int &k) {
-    using P = PipeTile;
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
     const int goff = tj.shared ? 0 : a.group_off[tj.g];
@@ -424,49 +428,47 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
     const int split = tj.shared ? a.split_s : a.split_r;
     const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
-    OperandRows rows;
+    // Both operands are affine: z rows rbase.. and W2 rows n0.. (z rows past
+    // the group are not fetched; W2 rows past d fetch row d - 1).
+    OperandRows<P> rows;
     rows.abase = (const uint16_t *)(tj.shared ? a.zs : a.zr) + rbase * K;
-#pragma unroll
-    for (int l = 0; l < P::A_LD; ++l) {
-        int r = P::load_row(threadIdx.x, l);
-        r = (r < tj.nrows) ? r : 0;
-        rows.aoff[l] = (uint32_t)r * (uint32_t)K;
-    }
-    rows.amask = valid_row_mask(tj.nrows);
+    const int r0 = P::load_row(threadIdx.x, 0);
+    rows.aoff[0] = (uint32_t)r0 * (uint32_t)K;
+    rows.astep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)K;
+    rows.amask = valid_row_mask<P>(tj.nrows);
     const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
     rows.bbase = tj.shared ? (const uint16_t *)a.w2s
                            : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
-#pragma unroll
-    for (int l = 0; l < P::B_LD; ++l) {
-        int n = n0 + P::load_row(threadIdx.x, l);
-        n = (n < a.d) ? n : a.d - 1;
-        rows.boff[l] = (uint32_t)n * (uint32_t)wk;
-    }
+    rows.boff[0] = (uint32_t)(n0 + r0) * (uint32_t)wk;
+    rows.bstep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)wk;
+    rows.bmask = valid_row_mask<P>(a.d - n0);
+    rows.blast = (uint32_t)(a.d - 1) * (uint32_t)wk;
     int my_pair = 0;
     float my_gate = 0.0f;
     if (!tj.shared && (int)threadIdx.x < tj.nrows) {
         my_pair = a.perm[rbase + threadIdx.x];
         my_gate = a.gsort[rbase + threadIdx.x];
     }
-    switch (wave_frags(tj.nrows)) {
-        case 4: return down_tile<4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 3: return down_tile<3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 2: return down_tile<2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 1: return down_tile<1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        default: return down_tile<0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+    switch (wave_frags<P>(tj.nrows)) {
+        case 4: return down_tile<P, 4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 3: return down_tile<P, 3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 2: return down_tile<P, 2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 1: return down_tile<P, 1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        default: return down_tile<P, 0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
     }
 }
 
-__global__ __launch_bounds__(PipeTile::NT) void k_down_bf16(const GroupedArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
+template <class P>
+__global__ __launch_bounds__(P::NT) void k_down_bf16(const GroupedArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
     int k = 0;
-    int item = publish_item(lds, a, k);
+    int item = publish_item<P>(lds, a, k);
     while (item >= 0) {
         int m, j;
         item_tile(a, item, m, j);
-        TileJob tj = row_tile(a, m, PipeTile::BM);
+        TileJob tj = row_tile(a, m, P::BM);
         tj.j = j;
-        item = down_body(a, tj, lds, k);
+        item = down_body<P>(a, tj, lds, k);
     }
 }
 
@@ -604,7 +606,7 @@ hipError_t launch_gate_up(const moe_config &c, const GroupedArgs &a0, hipStream_
         GroupedArgs a = a0;
         a.nt_routed = (c.d_ff + ts.bz1 - 1) / ts.bz1;
         a.nt_shared = (c.n_shared * c.d_ff_shared + ts.bz1 - 1) / ts.bz1;
-        hipLaunchKernelGGL(k_gate_up_bf16, dim3(grid), dim3(PipeTile::NT), 0, s, a);
+        hipLaunchKernelGGL(k_gate_up_bf16<PipeTile>, dim3(grid), dim3(PipeTile::NT), 0, s, a);
     }
     else
         hipLaunchKernelGGL(k_gate_up_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a0);
@@ -618,7 +620,7 @@ hipError_t launch_down(const moe_config &c, const GroupedArgs &a0, hipStream_t s
         const int grid = persistent_grid(1ll << 30, 1);
         GroupedArgs a = a0;
         a.nt_routed = a.nt_shared = (c.d_model + ts.bn2 - 1) / ts.bn2;
-        hipLaunchKernelGGL(k_down_bf16, dim3(grid), dim3(PipeTile::NT), 0, s, a);
+        hipLaunchKernelGGL(k_down_bf16<PipeTile>, dim3(grid), dim3(PipeTile::NT), 0, s, a);
     } else {
         hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(mt, 4)), dim3(256), 0, s, a0);
     }

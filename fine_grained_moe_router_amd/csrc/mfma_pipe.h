@@ -1,5 +1,5 @@
-// mfma_pipe.h -- the 256x256 bf16 MFMA tile engine of the grouped expert
-// GEMMs (gfx950).
+// mfma_pipe.h -- the bf16 MFMA tile engine of the grouped expert GEMMs and
+// the router GEMM (gfx950).
 //
 // C[256][256] = A[256][K] B[256][K]^T, both operands K-contiguous, fp32
 // accumulation with v_mfma_f32_32x32x16_bf16.  Eight waves, two per SIMD,
@@ -8,7 +8,10 @@
 // MFMA) nothing hides a wave's waits on its loads, LDS reads and barriers:
 // a skeleton of this pipeline with every operand in L2 ran at 1.72 us per
 // k-tile with one wave per SIMD and 1.37 us with two (the MFMAs alone take
-// 0.85 us).
+// 0.85 us).  A 384 x 256 tile (eight 96 x 128 waves, 17% fewer L2->LDS
+// bytes per multiply-add) was faster in a probe with its token rows in L2,
+// but its LDS holds only two weight stages, and with gathered token rows
+// its gate/up launch ran 4-8% slower than this tile's.
 //
 // Memory pipeline.  k-tiles of 64 values: each row contributes one whole
 // 128-byte cache line per k-tile (half-line requests halve the per-CU rate
@@ -38,7 +41,9 @@
 namespace moe {
 
 struct PipeTile {
-    static constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+    static constexpr int WM = 2, WN = 4;                   // wave grid
+    static constexpr int FM = 4, FN = 2;                   // 32x32 fragments per wave
+    static constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN, BK = 64, NT = 64 * WM * WN;
     static constexpr int A_STAGES = 2, B_STAGES = 3;
     static constexpr int CHUNKS = BK / 8;                  // 16-byte chunks per row
     static constexpr int A_LD = BM * CHUNKS / NT;          // global_load_lds per thread, A
@@ -46,8 +51,9 @@ struct PipeTile {
     static constexpr int A_STAGE = BM * CHUNKS * 16;       // bytes
     static constexpr int B_STAGE = BN * CHUNKS * 16;
     static constexpr int LDS_BYTES = A_STAGES * A_STAGE + B_STAGES * B_STAGE;
-    static constexpr int FM = 4, FN = 2;                   // 32x32 fragments per wave
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(NT == 512 && (BM * CHUNKS) % NT == 0 && (BN * CHUNKS) % NT == 0, "loads");
+    static_assert(FN % 2 == 0, "gate/up fragment pairs");
 
     __device__ static __forceinline__ int slot(int row, int chunk) {
         return chunk ^ ((row >> 1) & 7);
@@ -60,25 +66,47 @@ struct PipeTile {
     __device__ static __forceinline__ int load_chunk(int tid) {
         return slot(load_row(tid, 0), tid % CHUNKS);   // slot() is its own inverse
     }
-    // B tile row feeding fragment j of wave column wn (0..3).  SPLIT:
-    // fragment 0 comes from the first half (rows wn*32 ..), fragment 1 from
-    // the second half at the same offset.
+    // Wave coordinates (the same in every lane of a wave; read from lane 0
+    // so the compiler keeps them, and what derives from them, scalar).
+    __device__ static __forceinline__ int wave_m(int tid) {
+        return __builtin_amdgcn_readfirstlane((tid >> 6) % WM);
+    }
+    __device__ static __forceinline__ int wave_n(int tid) {
+        return __builtin_amdgcn_readfirstlane((tid >> 6) / WM);
+    }
+    // B tile row feeding fragment j of wave column wn.  SPLIT (gate/up): the
+    // tile's first BN/2 rows are W1 rows and the last BN/2 the W3 rows of the
+    // same hidden units; fragments j < FN/2 come from the first half and
+    // fragment j + FN/2 from the second half at the same offset, so
+    // fragments j and j + FN/2 hold the two halves of one SwiGLU.
     template <bool SPLIT>
     __device__ static __forceinline__ int b_row(int wn, int j) {
-        if (SPLIT) return (j == 0) ? wn * 32 : BN / 2 + wn * 32;
-        return wn * 64 + j * 32;
+        if (SPLIT) {
+            const int h = (j >= FN / 2) ? 1 : 0;
+            return h * (BN / 2) + (wn * (FN / 2) + j - h * (FN / 2)) * 32;
+        }
+        return (wn * FN + j) * 32;
     }
     // Tile row of fragment i of wave row wm.
-    __device__ static __forceinline__ int a_row(int wm, int i) { return (2 * i + wm) * 32; }
+    __device__ static __forceinline__ int a_row(int wm, int i) { return (WM * i + wm) * 32; }
 };
 
 // Row addresses of the rows one thread fetches: a uniform base plus 32-bit
-// element offsets (keeps the per-thread state small).
+// element offsets (keeps the per-thread state small).  Affine operands (the
+// rows of consecutive loads a fixed step apart) give only load 0's offset
+// and the step, which saves the vector registers of the others.
+template <class P>
 struct OperandRows {
     const uint16_t *abase, *bbase;
-    uint32_t aoff[PipeTile::A_LD];
-    uint32_t boff[PipeTile::B_LD];
-    uint32_t amask;   // bit n: A load n fetches a valid row (the rest are skipped)
+    uint32_t aoff[P::A_LD];
+    uint32_t boff[P::B_LD];
+    uint32_t astep, bstep;      // affine operands: element step from load n to n + 1
+    uint32_t amask;             // bit n: A load n fetches a valid row (the rest are skipped)
+    // Affine operands: bit n of bmask set when B load n fetches a valid row;
+    // the others fetch row blast (an element offset, the tile's last valid
+    // row) instead, so every B load is issued (the three-stage wait counts
+    // them).
+    uint32_t bmask, blast;
 };
 
 // Workgroup barrier without a memory fence.  __syncthreads() would also wait
@@ -104,29 +132,45 @@ __device__ __forceinline__ void load_lds16(const uint16_t *src, char *lds_dst) {
     __builtin_amdgcn_global_load_lds((const void *)src,
                                      (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
+// The same from a wave-uniform base plus a 32-bit byte offset: the form the
+// instruction takes natively (64-bit base in scalar registers, one vector
+// register of offset), so no 64-bit per-row address stays live in vector
+// registers across the K loop.  `base` must be the same in every lane.
+__device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint16_t *)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byte_off,
+                                              char *lds_dst) {
+    load_lds16((const uint16_t *)((const char *)base + byte_off), lds_dst);
+}
 
 // Run the K loop of one tile.  A rows past the valid count are not fetched
 // (rows.amask): their LDS rows keep stale values, which only reach output
-// rows that are discarded.  Every B row must be dereferenceable.  NF: how many of this wave's row fragments hold
-// a valid row (0..4) -- all waves run the same loads and barriers, a wave
-// with fewer valid fragments issues fewer MFMAs.  B's k offset of k-tile k0
-// is k0, or ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several
-// matrices side by side along K, possibly repeated).
-template <bool SPLIT, int NF>
-__device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows, int K, int bsplit,
-                                             int bmod, size_t bstride, int a_half,
-                                             f32x16 (&acc)[NF > 0 ? NF : 1][PipeTile::FN]) {
-    using P = PipeTile;
+// rows that are discarded.  Every B row must be dereferenceable.  NF: how
+// many of this wave's row fragments hold a valid row (0..FM) -- all waves
+// run the same loads and barriers, a wave with fewer valid fragments issues
+// fewer MFMAs.  B's k offset of k-tile k0 is k0, or
+// ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several matrices
+// side by side along K, possibly repeated).  AFF: both operands are affine
+// (rows.aoff[0], rows.astep; rows.boff[0], rows.bstep).
+template <class P, bool SPLIT, int NF, bool AFF = false>
+__device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &rows, int K,
+                                             int bsplit, int bmod, size_t bstride, int a_half,
+                                             f32x16 (&acc)[NF > 0 ? NF : 1][P::FN]) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = P::wave_m(tid);
+    const int wn = P::wave_n(tid);
     const int ca = P::load_chunk(tid) * 8;
     char *const a_lds = lds;
     char *const b_lds = lds + P::A_STAGES * P::A_STAGE;
+    constexpr int NA = NF > 0 ? NF : 1;
 #pragma unroll
-    for (int i = 0; i < (NF > 0 ? NF : 1); ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int j = 0; j < P::FN; ++j)
 #pragma unroll
@@ -144,52 +188,79 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
         return a_half ? (kt & 1) * a_half + (kt >> 1) * P::BK : kt * P::BK;
     };
     auto b_koff = [&](int kt) -> size_t { return koff_of((a_half ? kt >> 1 : kt) * P::BK); };
+    // Byte offsets (below 2^32: the API bounds every operand matrix to 2^31
+    // elements): row offset and chunk per thread, k offset per k-tile.  The
+    // bases are per tile, so the same in every lane; reading them from lane 0
+    // puts them in scalar registers even where the compiler cannot prove it.
+    const uint16_t *const abase = uniform_ptr(rows.abase);
+    const uint16_t *const bbase = uniform_ptr(rows.bbase);
+    constexpr int NAB = AFF ? 1 : P::A_LD, NBB = AFF ? 1 : P::B_LD;
+    uint32_t abyte[NAB], bbyte[NBB];
+#pragma unroll
+    for (int n = 0; n < NAB; ++n) abyte[n] = 2u * (rows.aoff[n] + (uint32_t)ca);
+#pragma unroll
+    for (int n = 0; n < NBB; ++n) bbyte[n] = 2u * (rows.boff[n] + (uint32_t)ca);
+    auto a_byte = [&](int n) -> uint32_t {
+        if constexpr (AFF) return abyte[0] + 2u * (uint32_t)n * rows.astep;
+        else return abyte[n];
+    };
+    uint32_t bclamp = 0;
+    if constexpr (AFF) bclamp = 2u * (rows.blast + (uint32_t)ca);
+    auto b_byte = [&](int n) -> uint32_t {
+        if constexpr (AFF)
+            return ((rows.bmask >> n) & 1) ? bbyte[0] + 2u * (uint32_t)n * rows.bstep : bclamp;
+        else return bbyte[n];
+    };
     auto a_load = [&](int n, int kt, int stage) {
         if ((rows.amask >> n) & 1)
-            load_lds16(rows.abase + rows.aoff[n] + a_col(kt) + ca,
-                       a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
+            load_lds16_at(abase, a_byte(n) + 2u * (uint32_t)a_col(kt),
+                          a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
     };
     auto b_load = [&](int n, size_t koff, int stage) {
-        load_lds16(rows.bbase + rows.boff[n] + koff + ca,
-                   b_lds + stage * P::B_STAGE + (n * P::NT + wave * 64) * 16);
+        load_lds16_at(bbase, b_byte(n) + 2u * (uint32_t)koff,
+                      b_lds + stage * P::B_STAGE + (n * P::NT + wave * 64) * 16);
     };
     const int nk = K / P::BK;
     // Prologue: A(0), B(0), B(1).  Every iteration kt then issues A(kt+1)
     // followed by B(kt+2), as far as they exist.  So at the top of iteration
     // kt < nk-1 the only loads issued after A(kt) and B(kt) are the B_LD
-    // loads of B(kt+1): vmcnt <= B_LD means both operands of k-tile kt have
-    // landed (vector memory loads complete in order); the last iteration
-    // has nothing in flight after them and waits for everything.
+    // loads of B(kt+1) (every B load is issued, see OperandRows): vmcnt <=
+    // B_LD means both operands of k-tile kt have landed (vector memory loads
+    // complete in order); the last iteration has nothing in flight after
+    // them and waits for everything.
+    static_assert(P::A_STAGES == 2 && P::B_STAGES == 3, "the waits below assume 2 + 3 stages");
+    constexpr int LB = P::B_STAGES - 1;
 #pragma unroll
     for (int n = 0; n < P::A_LD; ++n) a_load(n, 0, 0);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < LB; ++s) {
         if (s >= nk) break;
         const size_t ko = b_koff(s);
 #pragma unroll
         for (int n = 0; n < P::B_LD; ++n) b_load(n, ko, s);
     }
     constexpr int SUB = P::BK / 16;          // MFMA k-substeps per k-tile
-    constexpr int SLOTS = 4 * SUB;           // MFMA groups per k-tile
+    constexpr int GROUPS = P::FM;            // MFMA groups (one fragment row each) per substep
+    constexpr int SLOTS = SUB * GROUPS;
     constexpr int LOADS = P::A_LD + P::B_LD;
     for (int kt = 0; kt < nk; ++kt) {
         // A(kt) and B(kt) have landed (this thread's share) ...
         if (kt + 1 < nk) wait_vmcnt<P::B_LD>();
         else wait_vmcnt<0>();
         lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
-        const bool more_a = kt + 1 < nk, more_b = kt + 2 < nk;
+        const bool more_a = kt + 1 < nk, more_b = kt + LB < nk;
         const int ka = min(kt + 1, nk - 1);
-        const size_t kbo = b_koff(min(kt + 2, nk - 1));
+        const size_t kbo = b_koff(min(kt + LB, nk - 1));
         const int sa_next = (kt + 1) % P::A_STAGES;
-        const int sb_next = (kt + 2) % P::B_STAGES;
+        const int sb_next = (kt + LB) % P::B_STAGES;
         const u32x4 *Ab = (const u32x4 *)(a_lds + (kt % P::A_STAGES) * P::A_STAGE);
         const u32x4 *Bb = (const u32x4 *)(b_lds + (kt % P::B_STAGES) * P::B_STAGE);
-        bf16x8 a[2][NF > 0 ? NF : 1], b[2][P::FN];
-        auto frag_load = [&](int s, bf16x8 (&av)[NF > 0 ? NF : 1], bf16x8 (&bv)[P::FN]) {
+        bf16x8 a[2][NA], b[2][P::FN];
+        auto frag_load = [&](int s, bf16x8 (&av)[NA], bf16x8 (&bv)[P::FN]) {
             const int ch = 2 * s + (lane >> 5);
 #pragma unroll
             for (int j = 0; j < P::FN; ++j) {
-                const int row = P::b_row<SPLIT>(wn, j) + (lane & 31);
+                const int row = P::template b_row<SPLIT>(wn, j) + (lane & 31);
                 bv[j] = __builtin_bit_cast(bf16x8, Bb[row * P::CHUNKS + P::slot(row, ch)]);
             }
 #pragma unroll
@@ -201,20 +272,21 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
         frag_load(0, a[0], b[0]);
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
+            const int cur = s & 1;
             if (s + 1 < SUB) frag_load(s + 1, a[(s + 1) & 1], b[(s + 1) & 1]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < GROUPS; ++q) {
 #pragma unroll
                 for (int i = 0; i < NF; ++i)
                     if (i == q)
 #pragma unroll
                         for (int j = 0; j < P::FN; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+                                a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
                 // this group's share of the next loads, A loads first, then B
 #pragma unroll
                 for (int n = 0; n < LOADS; ++n) {
-                    if (n * SLOTS / LOADS != s * 4 + q) continue;
+                    if (n * SLOTS / LOADS != s * GROUPS + q) continue;
                     if (n < P::A_LD) {
                         if (more_a) a_load(n, ka, sa_next);
                     } else if (more_b) {
@@ -229,20 +301,24 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows &rows,
     lds_barrier();     // every wave done with the stages before the LDS is reused
 }
 
-// Bit n set when A load n of this thread fetches one of the nrows valid rows.
+// Bit n set when load n of this thread fetches one of the nrows valid rows
+// (A and B loads cover the rows alike).
+template <class P>
 __device__ __forceinline__ uint32_t valid_row_mask(int nrows) {
     uint32_t m = 0;
 #pragma unroll
-    for (int n = 0; n < PipeTile::A_LD; ++n)
-        m |= (PipeTile::load_row(threadIdx.x, n) < nrows ? 1u : 0u) << n;
+    for (int n = 0; n < P::A_LD; ++n)
+        m |= (P::load_row(threadIdx.x, n) < nrows ? 1u : 0u) << n;
     return m;
 }
 
-// Fragments (of 4) wave row wm must compute for a tile with nrows valid rows.
+// Fragments (of FM) this thread's wave row must compute for a tile with
+// nrows valid rows: those i with WM i + wm < ceil(nrows / 32).
+template <class P>
 __device__ __forceinline__ int wave_frags(int nrows) {
-    const int wm = (threadIdx.x >> 6) & 1;
+    const int wm = P::wave_m(threadIdx.x);
     const int nblk = (nrows + 31) >> 5;
-    return min(4, max(0, (nblk - wm + 1) >> 1));
+    return min(P::FM, max(0, (nblk - wm + P::WM - 1) / P::WM));
 }
 
 // Thread id the compiler cannot treat as loop-invariant: epilogue address
@@ -256,18 +332,18 @@ __device__ __forceinline__ int opaque_tid() {
 
 // Output coordinates of accumulator register r of fragment (i, j), given
 // tid = opaque_tid().
+template <class P>
 __device__ __forceinline__ int pipe_out_row(int tid, int i, int r) {
     const int lane = tid & 63;
-    const int wm = (tid >> 6) & 1;
-    return PipeTile::a_row(wm, i) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    return P::a_row(P::wave_m(tid), i) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
-// SPLIT: column within a half (the same for both fragments); else column of
-// the tile.
-template <bool SPLIT>
+// SPLIT: hidden column (within a half) of gate/up pair j (< FN/2); else
+// column of the tile.
+template <class P, bool SPLIT>
 __device__ __forceinline__ int pipe_out_col(int tid, int j) {
     const int lane = tid & 63;
-    const int wn = (tid >> 6) >> 1;
-    return SPLIT ? wn * 32 + (lane & 31) : wn * 64 + j * 32 + (lane & 31);
+    const int wn = P::wave_n(tid);
+    return SPLIT ? (wn * (P::FN / 2) + j) * 32 + (lane & 31) : (wn * P::FN + j) * 32 + (lane & 31);
 }
 
 }  // namespace moe

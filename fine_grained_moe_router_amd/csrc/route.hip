@@ -26,19 +26,19 @@ namespace moe {
 // with more it writes its partial sum to part[z] and k_router_reduce adds
 // them in split order.
 template <int NF>
-__device__ __forceinline__ void router_tile(char *lds, const OperandRows &rows, int K, int T,
+__device__ __forceinline__ void router_tile(char *lds, const OperandRows<PipeTile> &rows, int K, int T,
                                             int N, int m0, int n0, float *__restrict__ out) {
     f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
-    pipe_gemm_nf<false, NF>(lds, rows, K, 0, 1, 0, 0, acc);
+    pipe_gemm_nf<PipeTile, false, NF, true>(lds, rows, K, 0, 1, 0, 0, acc);
 #pragma unroll
     for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int j = 0; j < PipeTile::FN; ++j) {
             const int tid = opaque_tid();
-            const int col = n0 + pipe_out_col<false>(tid, j);
+            const int col = n0 + pipe_out_col<PipeTile, false>(tid, j);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + pipe_out_row(tid, i, r);
+                const int row = m0 + pipe_out_row<PipeTile>(tid, i, r);
                 if (row < T && col < N) out[(size_t)row * N + col] = acc[i][j][r];
             }
         }
@@ -55,21 +55,19 @@ __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int 
     const int K = min(d - k0, kps * P::BK);
     out += (size_t)blockIdx.z * T * N;
     const int nrows = min(P::BM, T - m0);
-    OperandRows rows;
+    // Both operands are affine: token rows m0.. and expert rows n0.. (token
+    // rows past T are not fetched; expert rows past N' fetch row N' - 1).
+    OperandRows<P> rows;
     rows.abase = x + k0;
     rows.bbase = wg + k0;
-#pragma unroll
-    for (int l = 0; l < P::A_LD; ++l) {
-        const int r = P::load_row(threadIdx.x, l);
-        rows.aoff[l] = (uint32_t)(m0 + (r < nrows ? r : 0)) * (uint32_t)d;   // rows past T: not fetched
-    }
-    rows.amask = valid_row_mask(nrows);
-#pragma unroll
-    for (int l = 0; l < P::B_LD; ++l) {
-        const int n = min(n0 + P::load_row(threadIdx.x, l), N - 1);   // experts past N': discarded
-        rows.boff[l] = (uint32_t)n * (uint32_t)d;
-    }
-    switch (wave_frags(nrows)) {
+    const int r0 = P::load_row(threadIdx.x, 0);
+    rows.aoff[0] = (uint32_t)(m0 + r0) * (uint32_t)d;
+    rows.boff[0] = (uint32_t)(n0 + r0) * (uint32_t)d;
+    rows.astep = rows.bstep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)d;
+    rows.amask = valid_row_mask<P>(nrows);
+    rows.bmask = valid_row_mask<P>(N - n0);
+    rows.blast = (uint32_t)(N - 1) * (uint32_t)d;
+    switch (wave_frags<P>(nrows)) {
         case 4: return router_tile<4>(lds, rows, K, T, N, m0, n0, out);
         case 3: return router_tile<3>(lds, rows, K, T, N, m0, n0, out);
         case 2: return router_tile<2>(lds, rows, K, T, N, m0, n0, out);

@@ -33,6 +33,13 @@ SMALL = {
         n_routed=8, top_k=8, n_shared=1, d_ff_shared=64),
     "f32_sigmoid": CONFIGS["toy_fp32"].with_(name="f32_sigmoid", T=200, scoring="sigmoid",
                                              renorm=True, bias=True),
+    # ~250 rows per routed expert (as at V3 prefill): experts spanning
+    # several row tiles, with ragged d (320) and d_ff (192)
+    "many_rows_ragged": scaled(CONFIGS["v3_prefill"], T=1000, d_model=320, d_ff=192).with_(
+        n_routed=16, top_k=4),
+    # ~375 rows per routed expert and two 64-wide shared experts side by side
+    "many_rows_two_shared": scaled(CONFIGS["mid"], T=1500, d_model=256, d_ff=128).with_(
+        n_routed=8, top_k=2, n_shared=2, d_ff_shared=64),
 }
 
 
@@ -173,6 +180,18 @@ def test_one_hot_expert_stealing_and_column_order():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+
+
+def test_one_hot_expert_few_experts():
+    """As above with 16 routed experts and 128-wide experts: expert 7 spans 8
+    row tiles, expert 3 four; the other 14 are empty."""
+    cfg = scaled(CONFIGS["v3_prefill"], T=2000, d_model=256, d_ff=128).with_(
+        n_routed=16, top_k=2)
+    idx = np.full((cfg.T, 2), -1, np.int32)
+    idx[:, 0] = 7
+    idx[::2, 1] = 3
+    gate = np.random.default_rng(4).random((cfg.T, 2)).astype(np.float32)
+    caller_routing_case(cfg, idx, gate)
 
 
 def test_many_experts_select_path():

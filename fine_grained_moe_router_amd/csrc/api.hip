@@ -104,6 +104,10 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which) {
     }
 }
 
+// The GEMMs move 16-byte chunks of every activation and weight row (rows
+// are multiples of 64 elements), and the combine 16 bytes of x and h.
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const float *logit_offset,
               const float *bias, const uint32_t *token_ids, float *logits, int32_t *topk_idx,
               float *topk_w, int32_t *expert_counts, void *p_partial, void *workspace,
@@ -127,6 +131,7 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const fl
         if (!logits) return MOE_ERR_INVALID_ARG;
     } else {
         if (!x || !w_gate) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_UNSUPPORTED;
         if (c.flags & MOE_LOGITS_OUT) {
             if (!logits) return MOE_ERR_INVALID_ARG;
         } else if (logits) {
@@ -157,6 +162,9 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     if (!x || !topk_idx || !topk_w || !w13 || !w2 || !h || !workspace) return MOE_ERR_INVALID_ARG;
     if (c.n_shared > 0 && (!w13_shared || !w2_shared)) return MOE_ERR_INVALID_ARG;
     if (h == x) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) ||
+        (c.n_shared > 0 && (!aligned16(w13_shared) || !aligned16(w2_shared))))
+        return MOE_ERR_UNSUPPORTED;
     const FwdLayout L = fwd_layout(c);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -276,7 +284,8 @@ const char *moe_status_string(int status) {
     switch (status) {
         case MOE_OK: return "ok";
         case MOE_ERR_INVALID_ARG: return "invalid argument";
-        case MOE_ERR_UNSUPPORTED: return "unsupported configuration (sizes must be multiples of 64)";
+        case MOE_ERR_UNSUPPORTED:
+            return "unsupported configuration (sizes must be multiples of 64, matrices 16-byte aligned)";
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_HIP: return hipGetErrorString(g_last_hip);
         default: return "unknown status";

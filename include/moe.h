@@ -16,7 +16,10 @@
  *    comment says otherwise.  The library never allocates or frees device
  *    memory: scratch lives in a caller-provided workspace of at least
  *    moe_workspace_bytes(cfg, which) bytes, 256-byte aligned.
- *  - Row-major layouts; "bf16" means IEEE bfloat16 bit patterns.
+ *  - Row-major layouts; "bf16" means IEEE bfloat16 bit patterns.  The
+ *    activation, weight and output matrices (x, w_gate, w13, w2, the shared
+ *    weights, h) must be 16-byte aligned (MOE_ERR_UNSUPPORTED otherwise);
+ *    allocator-returned buffers are.
  *  - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *    void*; NULL is the default stream).  Results are valid once the caller
  *    has synchronised that stream.
@@ -41,7 +44,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG (-1)   /* NULL pointer, bad size or mode        */
-#define MOE_ERR_UNSUPPORTED (-2)   /* valid but not implemented (alignment) */
+#define MOE_ERR_UNSUPPORTED (-2)   /* valid but not implemented (sizes, alignment) */
 #define MOE_ERR_WORKSPACE (-3)     /* workspace smaller than required       */
 #define MOE_ERR_HIP (-4)           /* a HIP launch or runtime call failed   */
 

@@ -129,6 +129,8 @@ def test_route_argument_errors(L):
     assert route(L, c, wg=None) == B.MOE_ERR_INVALID_ARG
     assert route(L, c, ws=None) == B.MOE_ERR_INVALID_ARG
     assert route(L, c, ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert route(L, c, x=ctypes.c_void_p(4096 + 8)) == B.MOE_ERR_UNSUPPORTED
+    assert route(L, c, wg=ctypes.c_void_p(4096 + 2)) == B.MOE_ERR_UNSUPPORTED
     assert route(L, c, logits=P) == B.MOE_ERR_INVALID_ARG      # logits given but no flag
     cin = cfg_of("v3_decode")
     cin.flags = B.LOGITS_IN
@@ -158,6 +160,10 @@ def test_forward_argument_errors(L):
     a = list(args)
     a[7] = a[0]                            # h aliases x
     assert L.moe_forward(ctypes.byref(c), *a, P, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    for i in (0, 3, 4, 5, 6, 7):          # matrices must be 16-byte aligned
+        a = list(args)
+        a[i] = ctypes.c_void_p(a[i].value + 8)
+        assert L.moe_forward(ctypes.byref(c), *a, P, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED, i
 
 
 def test_stats_argument_errors(L):

@@ -10,6 +10,8 @@
 
 namespace moe {
 
+constexpr int kMaxTopK = 16;   // the API's bound on K'
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int has_shared,
                                                  const void *__restrict__ x,
@@ -24,32 +26,59 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
     const int c = ((blockIdx.x % ncb) * blockDim.x + threadIdx.x) * 4;
     if (c >= d) return;
     const size_t o = (size_t)t * d + c;
+    // Every load is issued before the first add (K' <= kMaxTopK), so the
+    // K' + 2 reads of a thread overlap instead of waiting one by one.
+    uint2 xv = make_uint2(0, 0), sv = make_uint2(0, 0), yv[kMaxTopK];
+    float4 xf = make_float4(0, 0, 0, 0), sf = xf, yf[kMaxTopK];
+    bool live[kMaxTopK];
+    if constexpr (BF16) xv = *(const uint2 *)((const uint16_t *)x + o);
+    else xf = *(const float4 *)((const float *)x + o);
+    if (has_shared) {
+        if constexpr (BF16) sv = *(const uint2 *)(ysh + o);
+        else sf = *(const float4 *)(ys + o);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        live[k] = false;
+        if (k < K) {
+            const int e = idx[(size_t)t * K + k];
+            live[k] = e >= 0 && e < N;
+            const size_t oy = ((size_t)t * K + k) * d + c;
+            if (live[k]) {
+                if constexpr (BF16) yv[k] = *(const uint2 *)(yrh + oy);
+                else yf[k] = *(const float4 *)(yr + oy);
+            }
+        }
+    }
+    // fp16 values carrying the overflow mark are read from the fp32 array
+    auto staged = [&](uint2 p, const float *f32) -> float4 {
+        if (f16x4_marked(p)) return *(const float4 *)f32;
+        return make_float4(f16_lo(p.x), f16_hi(p.x), f16_lo(p.y), f16_hi(p.y));
+    };
     float4 acc;
-    if (BF16) {
-        const uint2 v = *(const uint2 *)((const uint16_t *)x + o);
-        acc.x = bf16_to_f32((uint16_t)(v.x & 0xffffu));
-        acc.y = bf16_to_f32((uint16_t)(v.x >> 16));
-        acc.z = bf16_to_f32((uint16_t)(v.y & 0xffffu));
-        acc.w = bf16_to_f32((uint16_t)(v.y >> 16));
+    if constexpr (BF16) {
+        acc.x = bf16_to_f32((uint16_t)(xv.x & 0xffffu));
+        acc.y = bf16_to_f32((uint16_t)(xv.x >> 16));
+        acc.z = bf16_to_f32((uint16_t)(xv.y & 0xffffu));
+        acc.w = bf16_to_f32((uint16_t)(xv.y >> 16));
     } else {
-        acc = *(const float4 *)((const float *)x + o);
+        acc = xf;
     }
     if (has_shared) {
-        const float4 s = BF16 ? f16x4_load(ysh + o, ys + o) : *(const float4 *)(ys + o);
-        acc.x += s.x;
-        acc.y += s.y;
-        acc.z += s.z;
-        acc.w += s.w;
+        const float4 v = BF16 ? staged(sv, ys + o) : sf;
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
     }
-    for (int k = 0; k < K; ++k) {
-        const int e = idx[(size_t)t * K + k];
-        if (e < 0 || e >= N) continue;
-        const size_t oy = ((size_t)t * K + k) * d + c;
-        const float4 y = BF16 ? f16x4_load(yrh + oy, yr + oy) : *(const float4 *)(yr + oy);
-        acc.x += y.x;
-        acc.y += y.y;
-        acc.z += y.z;
-        acc.w += y.w;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        if (!live[k]) continue;
+        const float4 v = BF16 ? staged(yv[k], yr + ((size_t)t * K + k) * d + c) : yf[k];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
     }
     if (BF16) {
         uint2 v;

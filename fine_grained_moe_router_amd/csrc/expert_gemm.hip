@@ -145,32 +145,45 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
 // every queue is drained.  Taking the ticket only when the block is free
 // (rather than one tile ahead) makes the order in which items start follow
 // the queue order, which keeps consecutive items close in time (EA read
-// traffic of the V3 gate/up launch 33.4 -> 31.1 GB).  The item (queue << 24
-// | index, or -1) reaches the other threads through one LDS word in the
+// traffic of the V3 gate/up launch 33.4 -> 31.1 GB).  The ticket's atomic
+// is issued right after the K loop and its result first used after the
+// epilogue's stores, so its latency hides behind them.  The item (queue <<
+// 24 | index, or -1) reaches the other threads through one LDS word in the
 // second A stage: after the K loop no wave reads that stage, and the next
 // tile first writes it after the top barrier of its first k-tile, which
 // every wave reaches only after it has read the word.
 constexpr int kItemBits = 24;
 static_assert(PipeTile::A_STAGES == 2, "queue slot lives in the second A stage");
 
-__device__ __forceinline__ int next_item(const GroupedArgs &a, int &k) {
+// Thread 0: the first ticket of a pull (a counter value; unused once every
+// queue is drained, k == kXcds).
+__device__ __forceinline__ int take_ticket(const GroupedArgs &a, int k) {
+    return (k < kXcds) ? atomicAdd(a.queue + (blockIdx.x % kXcds + k) % kXcds, 1) : 0;
+}
+// Thread 0: the item a pull ends with, from its first ticket; a ticket past
+// its queue's end moves on to the next queue with a new ticket.
+__device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int &k, int ticket) {
     const int x = blockIdx.x % kXcds;
     while (k < kXcds) {
         const int y = (x + k) % kXcds;
-        const int ticket = atomicAdd(a.queue + y, 1);
         if (ticket < xcd_queue(a, y).total) return (y << kItemBits) | ticket;
-        ++k;
+        if (++k < kXcds) ticket = atomicAdd(a.queue + (x + k) % kXcds, 1);
     }
     return -1;
 }
-// Called by every thread right after the K loop of a tile (and once before
-// the first tile).
+// Called by every thread with thread 0's first ticket of the pull; returns
+// the item to every thread.
 template <class P>
-__device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int &k) {
+__device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int &k, int ticket) {
     int32_t *slot = (int32_t *)(lds + P::A_STAGE);
-    if (threadIdx.x == 0) *slot = next_item(a, k);
+    if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
     lds_barrier();
     return __builtin_amdgcn_readfirstlane(*slot);
+}
+template <class P>
+__device__ __forceinline__ int first_item(char *lds, const GroupedArgs &a, int &k) {
+    const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
+    return publish_item<P>(lds, a, k, ticket);
 }
 __device__ __forceinline__ void item_tile(const GroupedArgs &a, int item, int &m, int &j) {
     const XcdQueue q = xcd_queue(a, item >> kItemBits);
@@ -225,7 +238,7 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
                                             size_t rbase, int &k) {
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
     pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
-    const int item = publish_item<P>(lds, a, k);
+    const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
     // split group the residual z - hi goes, rounded, zw columns further.
     // Four rows' z of one column are transposed across a lane quad so each
@@ -268,7 +281,7 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    return item;
+    return publish_item<P>(lds, a, k, ticket);
 }
 
 // Row tile m.  A group of cnt rows has R = ceil(cnt / bm) row tiles; its
@@ -338,7 +351,7 @@ template <class P>
 __global__ __launch_bounds__(P::NT) void k_gate_up_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
     int k = 0;
-    int item = publish_item<P>(lds, a, k);
+    int item = first_item<P>(lds, a, k);
     while (item >= 0) {
         int m, j;
         item_tile(a, item, m, j);
@@ -375,7 +388,8 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     int2 *info = (int2 *)(lds + row_info_offset<P>());
     if (!tj.shared && threadIdx.x < P::BM)
         info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
-    const int item = publish_item<P>(lds, a, k);   // its barrier also publishes info
+    lds_barrier();   // publishes info
+    const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
     // Four rows of one column are transposed across a lane quad: each lane
     // then stores four consecutive columns of one row, as fp16 (8 bytes; the
     // fp32 array only where fp16 overflows, see f16x4_store).
@@ -414,7 +428,7 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    return item;
+    return publish_item<P>(lds, a, k, ticket);
 }
 
 template <class P>
@@ -462,7 +476,7 @@ template <class P>
 __global__ __launch_bounds__(P::NT) void k_down_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
     int k = 0;
-    int item = publish_item<P>(lds, a, k);
+    int item = first_item<P>(lds, a, k);
     while (item >= 0) {
         int m, j;
         item_tile(a, item, m, j);

@@ -3,7 +3,7 @@
 //   h_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx[t][k]}(u_t)
 // The gate-scaled routed outputs arrive in pair order (t K' + k), the summed
 // shared output per token: fp32 for fp32 layers, fp16 for bf16 layers (with
-// fp32 kept where fp16 overflows; f16x4_load).  Each thread adds four columns
+// fp32 kept where fp16 overflows; f16x4_value).  Each thread adds four columns
 // in a fixed order (residual, shared, then k = 0..K'-1) in fp32 and rounds
 // once, so the result is the same bit pattern on every run (no atomics).
 #include "common.h"
@@ -50,11 +50,6 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
             }
         }
     }
-    // fp16 values carrying the overflow mark are read from the fp32 array
-    auto staged = [&](uint2 p, const float *f32) -> float4 {
-        if (f16x4_marked(p)) return *(const float4 *)f32;
-        return make_float4(f16_lo(p.x), f16_hi(p.x), f16_lo(p.y), f16_hi(p.y));
-    };
     float4 acc;
     if constexpr (BF16) {
         acc.x = bf16_to_f32((uint16_t)(xv.x & 0xffffu));
@@ -65,7 +60,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
         acc = xf;
     }
     if (has_shared) {
-        const float4 v = BF16 ? staged(sv, ys + o) : sf;
+        const float4 v = BF16 ? f16x4_value(sv, ys + o) : sf;
         acc.x += v.x;
         acc.y += v.y;
         acc.z += v.z;
@@ -74,7 +69,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
         if (!live[k]) continue;
-        const float4 v = BF16 ? staged(yv[k], yr + ((size_t)t * K + k) * d + c) : yf[k];
+        const float4 v = BF16 ? f16x4_value(yv[k], yr + ((size_t)t * K + k) * d + c) : yf[k];
         acc.x += v.x;
         acc.y += v.y;
         acc.z += v.z;

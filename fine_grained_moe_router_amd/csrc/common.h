@@ -33,34 +33,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // ---- fp16 staging of the expert outputs (bf16 layers) ----------------------
 // The gate-scaled expert outputs travel from the down projection to the
 // combine as fp16: 11 significant bits against bf16's 8, at half the bytes of
-// fp32.  A group of four values is stored as four halves.  When one of them
-// has no finite fp16 form (|v| >= 65520 rounds to infinity; NaN stays NaN),
-// its all-ones exponent marks the group, which is then also stored as fp32 at
-// the same index of an fp32 array, and the reader takes it from there.  So
-// the combine sees every value either as fp16(v) or as v itself.
-__device__ __forceinline__ uint32_t f16x2_pack(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
-}
+// fp32.  A value with no finite fp16 form (|v| >= 65520 rounds to infinity;
+// NaN stays NaN) keeps that non-finite half as a mark and is also written as
+// fp32 at the same index of an fp32 array, where the reader takes it from.
+// So the combine sees every value either as fp16(v) or as v itself.
 __device__ __forceinline__ float f16_lo(uint32_t p) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
 }
 __device__ __forceinline__ float f16_hi(uint32_t p) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
 }
+__device__ __forceinline__ bool f16_marked(uint32_t h) { return (h & 0x7C00u) == 0x7C00u; }
 __device__ __forceinline__ bool f16x4_marked(uint2 p) {
     return ((p.x & 0x7C00u) == 0x7C00u) | ((p.x & 0x7C000000u) == 0x7C000000u) |
            ((p.y & 0x7C00u) == 0x7C00u) | ((p.y & 0x7C000000u) == 0x7C000000u);
 }
-__device__ __forceinline__ void f16x4_store(uint16_t *h, float *f, float4 v) {
-    const uint2 p = make_uint2(f16x2_pack(v.x, v.y), f16x2_pack(v.z, v.w));
-    *(uint2 *)h = p;
-    if (f16x4_marked(p)) *(float4 *)f = v;
-}
-__device__ __forceinline__ float4 f16x4_load(const uint16_t *h, const float *f) {
-    const uint2 p = *(const uint2 *)h;
-    if (f16x4_marked(p)) return *(const float4 *)f;
-    return make_float4(f16_lo(p.x), f16_hi(p.x), f16_lo(p.y), f16_hi(p.y));
+// Four staged values (p: their halves, f: the same four slots of the fp32
+// array).
+__device__ __forceinline__ float4 f16x4_value(uint2 p, const float *f) {
+    float4 v = make_float4(f16_lo(p.x), f16_hi(p.x), f16_lo(p.y), f16_hi(p.y));
+    if (f16x4_marked(p)) {
+        if (f16_marked(p.x)) v.x = f[0];
+        if (f16_marked(p.x >> 16)) v.y = f[1];
+        if (f16_marked(p.y)) v.z = f[2];
+        if (f16_marked(p.y >> 16)) v.w = f[3];
+    }
+    return v;
 }
 
 // ---- wave reductions (64 lanes) --------------------------------------------
@@ -145,7 +143,7 @@ struct GroupedArgs {
     const void *x, *w13, *w2, *w13s, *w2s;
     void *zr, *zs;
     float *yr, *ys;
-    uint16_t *yrh, *ysh;      // fp16 outputs of the bf16 kernels (see f16x4_store)
+    uint16_t *yrh, *ysh;      // fp16 outputs of the bf16 kernels (see f16x4_value)
 };
 
 // ---- launchers (each returns hipSuccess or the launch error) ---------------

@@ -149,11 +149,25 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
 // is issued right after the K loop and its result first used after the
 // epilogue's stores, so its latency hides behind them.  The item (queue <<
 // 24 | index, or -1) reaches the other threads through one LDS word in the
-// second A stage: after the K loop no wave reads that stage, and the next
-// tile first writes it after the top barrier of its first k-tile, which
-// every wave reaches only after it has read the word.
+// last B stage, after the down projection's row info (tile_info_offset):
+// after the K loop no wave reads that stage (the epilogues stage their
+// tiles in the others), and the next tile first writes it after the top
+// barrier of its first k-tile, which every wave reaches only after it has
+// read the word.
 constexpr int kItemBits = 24;
-static_assert(PipeTile::A_STAGES == 2, "queue slot lives in the second A stage");
+
+// Row info of a down tile (pair id and gate of each of its rows) and then
+// the queue word, in the last B stage.
+template <class P>
+constexpr int tile_info_offset() {
+    static_assert(P::NT >= P::BM, "one tile row per thread");
+    static_assert(P::BM * 8 + 4 <= P::B_STAGE, "row info and queue word fit one B stage");
+    static_assert(P::A_STAGES * P::A_STAGE + (P::B_STAGES - 1) * P::B_STAGE >= P::BM * P::BN * 2,
+                  "an fp16 output tile fits the stages before the last");
+    return P::A_STAGES * P::A_STAGE + (P::B_STAGES - 1) * P::B_STAGE;
+}
+template <class P>
+constexpr int queue_slot_offset() { return tile_info_offset<P>() + 8 * P::BM; }
 
 // Thread 0: the first ticket of a pull (a counter value; unused once every
 // queue is drained, k == kXcds).
@@ -175,7 +189,7 @@ __device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int &k, int 
 // the item to every thread.
 template <class P>
 __device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int &k, int ticket) {
-    int32_t *slot = (int32_t *)(lds + P::A_STAGE);
+    int32_t *slot = (int32_t *)(lds + queue_slot_offset<P>());
     if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
     lds_barrier();
     return __builtin_amdgcn_readfirstlane(*slot);
@@ -361,20 +375,21 @@ __global__ __launch_bounds__(P::NT) void k_gate_up_bf16(const GroupedArgs a) {
     }
 }
 
-// (pair, gate) of row t of a routed down tile sits in LDS word pair t of
-// the last B stage, which no wave reads after the K loop and which the next
-// tile first writes after the top barrier of its first k-tile (its prologue
-// fills the B stages before the last).
+// Byte offset of (row, col) in an fp16 output tile staged in LDS: rows of
+// BN halves; the 16-byte chunk c of row r sits at chunk c ^ (4 ((r >> 2) & 1)),
+// so the two row groups one staging write covers (lanes 0-31: rows r..,
+// lanes 32-63: rows r + 4..) fall in disjoint LDS banks.
 template <class P>
-constexpr int row_info_offset() {
-    static_assert(P::NT >= P::BM, "one tile row per thread");
-    static_assert(P::BM * 8 <= P::B_STAGE, "row info fits one B stage");
-    return P::A_STAGES * P::A_STAGE + (P::B_STAGES - 1) * P::B_STAGE;
+__device__ __forceinline__ int stage_offset(int row, int col) {
+    return 2 * (row * P::BN + ((((col >> 3) ^ (((row >> 2) & 1) << 2))) << 3) + (col & 7));
 }
 
 // One down-projection tile whose wave computes NF row fragments.  Thread t
-// brings the pair id and gate of tile row t (fetched before the K loop); the
-// epilogue reads them back from LDS, so its stores never wait on a load.
+// brings the destination row and gate of tile row t (fetched before the K
+// loop).  Epilogue: every wave writes fp16(gate * y) of its fragments into
+// the tile staged in LDS (the A stages and the first two B stages), then
+// each wave stores two whole rows of 512 bytes at a time with 16-byte lane
+// stores.  A value beyond fp16's range (rare) is also stored as fp32.
 template <class P, int NF>
 __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                          const OperandRows<P> &rows, int K, int split, int n0,
@@ -385,47 +400,73 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
                                          split ? K / 2 : 0, acc);
     else
         pipe_gemm_nf<P, false, NF, true>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
-    int2 *info = (int2 *)(lds + row_info_offset<P>());
-    if (!tj.shared && threadIdx.x < P::BM)
-        info[threadIdx.x] = make_int2(my_pair, __float_as_int(my_gate));
-    lds_barrier();   // publishes info
+    int32_t *rdst = (int32_t *)(lds + tile_info_offset<P>());   // destination row
+    float *rgate = (float *)(lds + tile_info_offset<P>() + 4 * P::BM);
+    if (threadIdx.x < P::BM) {
+        rdst[threadIdx.x] = tj.shared ? tj.row0 + (int)threadIdx.x : my_pair;
+        rgate[threadIdx.x] = tj.shared ? 1.0f : my_gate;
+    }
+    lds_barrier();   // publishes the row info
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
-    // Four rows of one column are transposed across a lane quad: each lane
-    // then stores four consecutive columns of one row, as fp16 (8 bytes; the
-    // fp32 array only where fp16 overflows, see f16x4_store).
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    char *const st = lds;
+    uint32_t hmax = 0;   // largest |half| of a valid row: 0x7C00 and up = not finite
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
+        const int rb = P::a_row(P::wave_m(tid), i) + (lane >> 5) * 4;   // + 8 q + s
+        float g[16];
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const int tid = opaque_tid();
-            const int row = quad_row<P>(tid, i, rq);
-            size_t o = 0;
-            bool live = false, shared = tj.shared;
-            float gate = 1.0f;
-            if (row < tj.nrows) {
-                live = true;
-                if (shared) {
-                    o = (size_t)(tj.row0 + row) * a.d;
-                } else {
-                    const int2 v = info[row];
-                    gate = __int_as_float(v.y);
-                    o = (size_t)v.x * a.d;
-                }
+        for (int q = 0; q < 4; ++q) {
+            const float4 gq = *(const float4 *)(rgate + rb + 8 * q);
+            g[4 * q] = gq.x;
+            g[4 * q + 1] = gq.y;
+            g[4 * q + 2] = gq.z;
+            g[4 * q + 3] = gq.w;
+        }
+#pragma unroll
+        for (int j = 0; j < P::FN; ++j) {
+            const int col = pipe_out_col<P, false>(tid, j);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = rb + 8 * (r >> 2) + (r & 3);
+                const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(g[r] * acc[i][j][r]));
+                hmax = max(hmax, row < tj.nrows ? (h & 0x7FFFu) : 0u);
+                *(uint16_t *)(st + stage_offset<P>(row, col)) = (uint16_t)h;
             }
-            float *dst = shared ? a.ys + o : a.yr + o;
-            uint16_t *dsth = shared ? a.ysh + o : a.yrh + o;
+        }
+    }
+    const int ncols = min(P::BN, a.d - n0);
+    if (hmax >= 0x7C00u) {
+        // some value of this lane has no finite fp16 form: store it as fp32
+        float *yf = tj.shared ? a.ys : a.yr;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int rb = P::a_row(P::wave_m(tid), i) + (lane >> 5) * 4;
 #pragma unroll
             for (int j = 0; j < P::FN; ++j) {
-                float v[4];
+                const int col = pipe_out_col<P, false>(tid, j);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * rq + q];
-                quad_transpose(v, tid & 3);
-                const int col = n0 + (pipe_out_col<P, false>(tid, j) & ~3);
-                if (live && col < a.d)
-                    f16x4_store(dsth + col, dst + col,
-                                make_float4(gate * v[0], gate * v[1], gate * v[2], gate * v[3]));
+                for (int r = 0; r < 16; ++r) {
+                    const int row = rb + 8 * (r >> 2) + (r & 3);
+                    const float w = rgate[row] * acc[i][j][r];
+                    if (row < tj.nrows && col < ncols &&
+                        f16_marked(__builtin_bit_cast(uint16_t, (_Float16)w)))
+                        yf[(size_t)rdst[row] * a.d + n0 + col] = w;
+                }
             }
-            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    lds_barrier();   // the staged tile is complete
+    uint16_t *yh = tj.shared ? a.ysh : a.yrh;
+    constexpr int CHUNKS = P::BN / 8;   // 16-byte chunks per row
+#pragma unroll 4
+    for (int it = 0; it < P::BM * CHUNKS / P::NT; ++it) {
+        const int q = it * P::NT + tid;
+        const int row = q / CHUNKS, c8 = (q % CHUNKS) * 8;
+        if (row < tj.nrows && c8 < ncols) {
+            const uint4 v = *(const uint4 *)(st + stage_offset<P>(row, c8));
+            *(uint4 *)(yh + (size_t)rdst[row] * a.d + n0 + c8) = v;
         }
     }
     return publish_item<P>(lds, a, k, ticket);

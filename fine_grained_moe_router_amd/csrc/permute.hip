@@ -87,23 +87,34 @@ __global__ __launch_bounds__(256) void k_perm_hist(int P, int N, int chunk,
     for (int e = threadIdx.x; e < N; e += blockDim.x) cc[(size_t)blockIdx.x * N + e] = h[e];
 }
 
-// Exclusive scan of data[0..n) (n <= 2 * blockDim.x) held in LDS; returns the
-// total.  tmp: blockDim.x ints of LDS.
+// Exclusive scan of data[0..n) (n <= 2 * blockDim.x, blockDim.x a multiple
+// of 64) held in LDS; returns the total.  Each thread adds a pair, each
+// wavefront scans its 64 pair sums with lane shuffles, and the first
+// wavefront scans the wavefront totals: four barriers in all.  tmp:
+// blockDim.x / 64 ints of LDS.
 __device__ int block_excl_scan(int32_t *data, int n, int32_t *tmp) {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
     const int a = (2 * t < n) ? data[2 * t] : 0;
     const int b = (2 * t + 1 < n) ? data[2 * t + 1] : 0;
-    tmp[t] = a + b;
-    __syncthreads();
-    for (int o = 1; o < (int)blockDim.x; o <<= 1) {
-        const int v = (t >= o) ? tmp[t - o] : 0;
-        __syncthreads();
-        tmp[t] += v;
-        __syncthreads();
+    int v = a + b;   // inclusive scan of the pair sums within the wavefront
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
     }
-    const int excl = tmp[t] - (a + b);
-    const int total = tmp[blockDim.x - 1];
+    if (lane == 63) tmp[w] = v;
     __syncthreads();
+    if (w == 0) {    // inclusive scan of the wavefront totals
+        int s = (lane < nw) ? tmp[lane] : 0;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(s, o, 64);
+            if (lane >= o) s += u;
+        }
+        if (lane < nw) tmp[lane] = s;
+    }
+    __syncthreads();
+    const int excl = (w ? tmp[w - 1] : 0) + v - (a + b);
+    const int total = tmp[nw - 1];
+    __syncthreads();   // tmp is free again
     if (2 * t < n) data[2 * t] = excl;
     if (2 * t + 1 < n) data[2 * t + 1] = excl + a;
     __syncthreads();

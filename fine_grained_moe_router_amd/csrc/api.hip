@@ -32,10 +32,10 @@ struct StageScope {
         if (!g_prof.on || g_prof.used >= g_prof.cap) return;
         idx = g_prof.used++;
         g_prof.stage[idx] = stage;
-        hipEventRecord(g_prof.ev[2 * idx], s);
+        (void)hipEventRecord(g_prof.ev[2 * idx], s);
     }
     ~StageScope() {
-        if (idx >= 0) hipEventRecord(g_prof.ev[2 * idx + 1], s);
+        if (idx >= 0) (void)hipEventRecord(g_prof.ev[2 * idx + 1], s);
     }
 };
 

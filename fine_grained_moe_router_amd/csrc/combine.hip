@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
     const int ncb = (d / 4 + blockDim.x - 1) / blockDim.x;
     const int t = blockIdx.x / ncb;
     const int c = ((blockIdx.x % ncb) * blockDim.x + threadIdx.x) * 4;
-    if (c >= d) return;
+    if (t >= T || c >= d) return;
     const size_t o = (size_t)t * d + c;
     // Every load is issued before the first add (K' <= kMaxTopK), so the
     // K' + 2 reads of a thread overlap instead of waiting one by one.

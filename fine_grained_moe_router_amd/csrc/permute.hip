@@ -197,10 +197,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(int N, int n_chunks, int32_t
 
 // One block.  Computes group row counts/offsets, the tile prefix sums of
 // both GEMMs, the row-tile prefix sums and the per-XCD row-tile ranges.
-__global__ __launch_bounds__(1024) void k_perm_scan(int N, int n_chunks, int T, int n_shared,
-                                                    int f, int fsum, int d, int split_r,
-                                                    int split_s, TileShape ts,
-                                                    int32_t *__restrict__ cc,
+__global__ __launch_bounds__(1024) void k_perm_scan(int N, int T, int n_shared, int f, int fsum,
+                                                    int d, int split_r, int split_s, TileShape ts,
                                                     int32_t *__restrict__ meta,
                                                     int32_t *__restrict__ rtg) {
     __shared__ int32_t cnt[2048], t1[2048], t2[2048], tmp[1024];
@@ -296,10 +294,9 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
                        idx, cc, meta + mi.bad);
     hipLaunchKernelGGL(k_chunk_scan, dim3(N), dim3(256), 0, s, N, L.n_chunks, cc,
                        meta + mi.group_cnt);
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, L.n_chunks, c.T, c.n_shared,
-                       c.d_ff, c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
-                       z_split_shared(c) ? 1 : 0, tile_shape(c), cc, meta,
-                       (int32_t *)(ws + L.off_rtg));
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, c.T, c.n_shared, c.d_ff,
+                       c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
+                       z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (int32_t *)(ws + L.off_rtg));
     hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
                        L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
                        (float *)(ws + L.off_gsort));

@@ -77,8 +77,8 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int K, int N, int
     }
     if (BF16) {
         uint2 v;
-        v.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-        v.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+        v.x = pack_bf16x2(acc.x, acc.y);
+        v.y = pack_bf16x2(acc.z, acc.w);
         *(uint2 *)((uint16_t *)h + o) = v;
     } else {
         *(float4 *)((float *)h + o) = acc;

@@ -240,8 +240,8 @@ __device__ __forceinline__ int quad_row(int tid, int i, int rq) {
 
 __device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
     uint2 o;
-    o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
     return o;
 }
 
@@ -253,7 +253,9 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
     pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
-    // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u), rounded to bf16 (hi); for a
+    // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u) (the sigmoid from the hardware
+    // exponential and reciprocal, each within about an ulp of fp32; z is
+    // rounded to bf16 next), rounded to bf16 (hi); for a
     // split group the residual z - hi goes, rounded, zw columns further.
     // Four rows' z of one column are transposed across a lane quad so each
     // lane stores four consecutive columns of one row (8 bytes).
@@ -273,7 +275,7 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
                 for (int q = 0; q < 4; ++q) {
                     const float ga = acc[i][jp][4 * rq + q];              // W1 (gate) fragment
                     const float up = acc[i][jp + P::FN / 2][4 * rq + q];  // W3 (up) fragment
-                    z[q] = ga / (1.0f + __expf(-ga)) * up;
+                    z[q] = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * up;
                 }
                 quad_transpose(z, tid & 3);
                 const int row = quad_row<P>(tid, i, rq);

@@ -249,7 +249,18 @@ def test_full_size_workload(name):
     launches them: routing of every token checked bit-exactly on identical
     logits, the layer output checked on sampled tokens (all of them for the
     64-token decode batch)."""
-    cfg = CONFIGS[name]
+    full_size_check(CONFIGS[name])
+
+
+def test_large_batch():
+    """The V3 layer at T = 65536: 524,288 pairs (8 times the benchmark's
+    batch), about 2,300 row tiles per GEMM and 2,048-pair permutation
+    chunks.  Checked as the full-size workloads are."""
+    full_size_check(CONFIGS["v3_prefill"].with_(name="v3_T65536", T=65536))
+
+
+def full_size_check(cfg):
+    name = cfg.name
     print(f"[full-size] {name}: generating inputs", flush=True)
     inp = make_inputs(cfg, "cuda")
     print(f"[full-size] {name}: GPU layer", flush=True)

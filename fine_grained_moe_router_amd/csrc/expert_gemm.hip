@@ -338,6 +338,7 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
         rows.aoff[l] = (uint32_t)tok * (uint32_t)a.d;
     }
     rows.amask = valid_row_mask<P>(tj.nrows);
+    rows.azero = pad_row_mask<P>(tj.nrows);
     // B rows: hidden columns zc0 .. zc0+127 of W1 (tile rows 0..127) and of
     // W3 (tile rows 128..255); the shared group's hidden columns run across
     // its K_s experts.
@@ -493,6 +494,7 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
     rows.aoff[0] = (uint32_t)r0 * (uint32_t)K;
     rows.astep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)K;
     rows.amask = valid_row_mask<P>(tj.nrows);
+    rows.azero = pad_row_mask<P>(tj.nrows);
     const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
     rows.bbase = tj.shared ? (const uint16_t *)a.w2s
                            : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;

@@ -102,6 +102,10 @@ struct OperandRows {
     uint32_t boff[P::B_LD];
     uint32_t astep, bstep;      // affine operands: element step from load n to n + 1
     uint32_t amask;             // bit n: A load n fetches a valid row (the rest are skipped)
+    // bit n: A load n's row is past the valid rows but inside a fragment the
+    // tile computes; its LDS slot is zeroed in both A stages instead, so the
+    // MFMAs over it multiply zeros (less power than stale values)
+    uint32_t azero = 0;
     // Affine operands: bit n of bmask set when B load n fetches a valid row;
     // the others fetch row blast (an element offset, the tile's last valid
     // row) instead, so every B load is issued (the three-stage wait counts
@@ -221,6 +225,12 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
                       b_lds + stage * P::B_STAGE + (n * P::NT + wave * 64) * 16);
     };
     const int nk = K / P::BK;
+#pragma unroll
+    for (int n = 0; n < P::A_LD; ++n)
+        if ((rows.azero >> n) & 1)
+#pragma unroll
+            for (int st = 0; st < P::A_STAGES; ++st)
+                *(u32x4 *)(a_lds + st * P::A_STAGE + (n * P::NT + tid) * 16) = u32x4{0, 0, 0, 0};
     // Prologue: A(0), B(0), B(1).  Every iteration kt then issues A(kt+1)
     // followed by B(kt+2), as far as they exist.  So at the top of iteration
     // kt < nk-1 the only loads issued after A(kt) and B(kt) are the B_LD
@@ -310,6 +320,14 @@ __device__ __forceinline__ uint32_t valid_row_mask(int nrows) {
     for (int n = 0; n < P::A_LD; ++n)
         m |= (P::load_row(threadIdx.x, n) < nrows ? 1u : 0u) << n;
     return m;
+}
+
+// Bits of the A loads whose rows lie past nrows but inside the last 32-row
+// fragment a tile with nrows valid rows computes.
+template <class P>
+__device__ __forceinline__ uint32_t pad_row_mask(int nrows) {
+    const int computed = min(P::BM, (nrows + 31) & ~31);
+    return valid_row_mask<P>(computed) & ~valid_row_mask<P>(nrows);
 }
 
 // Fragments (of FM) this thread's wave row must compute for a tile with

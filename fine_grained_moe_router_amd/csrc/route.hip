@@ -65,6 +65,7 @@ __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int 
     rows.boff[0] = (uint32_t)(n0 + r0) * (uint32_t)d;
     rows.astep = rows.bstep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)d;
     rows.amask = valid_row_mask<P>(nrows);
+    rows.azero = pad_row_mask<P>(nrows);
     rows.bmask = valid_row_mask<P>(N - n0);
     rows.blast = (uint32_t)(N - 1) * (uint32_t)d;
     switch (wave_frags<P>(nrows)) {

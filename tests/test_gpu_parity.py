@@ -37,6 +37,9 @@ SMALL = {
     # several row tiles, with ragged d (320) and d_ff (192)
     "many_rows_ragged": scaled(CONFIGS["v3_prefill"], T=1000, d_model=320, d_ff=192).with_(
         n_routed=16, top_k=4),
+    # the largest K' the API takes (16): the select kernel's and the
+    # combine's per-token bounds
+    "top16": scaled(CONFIGS["mid"], T=300, d_model=256, d_ff=64).with_(top_k=16),
     # ~375 rows per routed expert and two 64-wide shared experts side by side
     "many_rows_two_shared": scaled(CONFIGS["mid"], T=1500, d_model=256, d_ff=128).with_(
         n_routed=8, top_k=2, n_shared=2, d_ff_shared=64),

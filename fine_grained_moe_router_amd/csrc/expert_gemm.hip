@@ -26,8 +26,6 @@
 
 namespace moe {
 
-enum { kGateUp = 0, kDown = 1 };
-
 __device__ __forceinline__ int find_group(const int32_t *__restrict__ base, int G, int tile) {
     int lo = 0, hi = G;  // base[lo] <= tile < base[hi]
     while (hi - lo > 1) {
@@ -229,9 +227,9 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int p) {
     }
 }
 
-// Epilogue coordinates after quad_transpose of accumulator registers
-// 4 rq .. 4 rq + 3 of fragment i: the lane's output row, and the first of
-// its four consecutive columns relative to the fragment's column block.
+// Output row of a lane after quad_transpose of accumulator registers
+// 4 rq .. 4 rq + 3 of fragment i (its four consecutive columns start at
+// pipe_out_col(tid, j) & ~3).
 template <class P>
 __device__ __forceinline__ int quad_row(int tid, int i, int rq) {
     const int lane = tid & 63;
@@ -253,10 +251,10 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
     pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
-    // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u) (the sigmoid from the hardware
-    // exponential and reciprocal, each within about an ulp of fp32; z is
-    // rounded to bf16 next), rounded to bf16 (hi); for a
-    // split group the residual z - hi goes, rounded, zw columns further.
+    // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u) in fp32 (the sigmoid from the
+    // hardware exponential and reciprocal, each within about an ulp), rounded
+    // to bf16 (hi); for a split group the residual z - hi goes, rounded, zw
+    // columns further.
     // Four rows' z of one column are transposed across a lane quad so each
     // lane stores four consecutive columns of one row (8 bytes).
     uint16_t *zout = (uint16_t *)(tj.shared ? a.zs : a.zr);

@@ -92,6 +92,8 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed timing of the same step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--pmc-run", action="store_true",
@@ -143,6 +145,29 @@ class Layer:
         B.balance_stats(cfg, r["counts"], r["pstat"], want_P=not hashed, want_loss=not hashed,
                         out=self.stats_out)
         return r
+
+
+def graph_step_ms(layer, steps: int) -> float:
+    """The same step captured once in a HIP graph and replayed: ms per
+    replay over `steps` replays (no launch overhead between the kernels).
+    Reported beside the eagerly launched step, which `value` is."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.step()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / steps
 
 
 def cpu_baseline(layer, target_s: float):
@@ -405,6 +430,7 @@ def main(argv=None):
     t1 = time.perf_counter()
     stages = B.profile_collect()
     ms = (t1 - t0) * 1000.0 / args.steps
+    graph_ms = None if args.no_graph else graph_step_ms(layer, args.steps)
 
     counts = layer.route_out["counts"].cpu()
     touched = int((counts > 0).sum())
@@ -453,6 +479,7 @@ def main(argv=None):
                   "experts_touched": touched,
                   "max_over_mean_load": float(counts.max()) / max(float(counts.float().mean()), 1e-9)},
         "stages_ms": stage_ms,
+        "graph_ms_per_step": graph_ms,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -37,6 +37,8 @@ SMALL = {
     # several row tiles, with ragged d (320) and d_ff (192)
     "many_rows_ragged": scaled(CONFIGS["v3_prefill"], T=1000, d_model=320, d_ff=192).with_(
         n_routed=16, top_k=4),
+    # the smallest sizes the API takes (d = d_ff = 64): one k-tile per K loop
+    "d64": scaled(CONFIGS["v3_prefill"], T=100, d_model=64, d_ff=64),
     # the largest K' the API takes (16): the select kernel's and the
     # combine's per-token bounds
     "top16": scaled(CONFIGS["mid"], T=300, d_model=256, d_ff=64).with_(top_k=16),

@@ -411,6 +411,35 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
     const int tid = opaque_tid();
     const int lane = tid & 63;
+    const int ncols = min(P::BN, a.d - n0);
+    if (tj.nrows <= 8) {
+        // A tile of at most 8 rows (decode-sized groups): they all sit in
+        // accumulator registers 0-3 of fragment 0 of wave row 0 (rows 0-3 in
+        // lanes 0-31, rows 4-7 in lanes 32-63), stored directly, 2 bytes a
+        // lane, with no staging.
+        if (NF > 0 && P::wave_m(tid) == 0) {
+            uint16_t *yh = tj.shared ? a.ysh : a.yrh;
+            float *yf = tj.shared ? a.ys : a.yr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = (lane >> 5) * 4 + r;
+                if (row >= tj.nrows) continue;
+                const float g = rgate[row];
+                const size_t o = (size_t)rdst[row] * a.d + n0;
+#pragma unroll
+                for (int j = 0; j < P::FN; ++j) {
+                    const int col = pipe_out_col<P, false>(tid, j);
+                    const float w = g * acc[0][j][r];
+                    const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)w);
+                    if (col < ncols) {
+                        yh[o + col] = h;
+                        if (f16_marked(h)) yf[o + col] = w;
+                    }
+                }
+            }
+        }
+        return publish_item<P>(lds, a, k, ticket);
+    }
     char *const st = lds;
     uint32_t hmax = 0;   // largest |half| of a valid row: 0x7C00 and up = not finite
 #pragma unroll
@@ -437,7 +466,6 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
             }
         }
     }
-    const int ncols = min(P::BN, a.d - n0);
     if (hmax >= 0x7C00u) {
         // some value of this lane has no finite fp16 form: store it as fp32
         float *yf = tj.shared ? a.ys : a.yr;

@@ -85,7 +85,7 @@ struct FwdLayout {
     size_t off_meta;    // int32 meta block (see MetaIdx)
     size_t off_perm;    // int32 [T*K']: pair id at each expert-ordered row
     size_t off_gsort;   // fp32 [T*K']: gate of each expert-ordered row
-    size_t off_rtg;     // int32 [max_row_tiles]: group of each 256-row tile
+    size_t off_rtg;     // RowTileDesc [max_row_tiles]: the group of each 256-row tile
     int max_row_tiles;  // bound on the row tiles of all groups
     size_t off_zr;      // [T*K'][d_ff] dtype: routed hidden activations
     size_t off_zs;      // [T][K_s*d_ff_shared] dtype: shared hidden activations
@@ -129,6 +129,18 @@ struct TileShape {
     int bm2, bn2;  // down GEMM: rows per tile, output columns per tile
 };
 
+// The group of a row tile of the bf16 GEMMs, in one 32-byte record (written
+// by the permutation for every row tile of the group), so an item resolves
+// to its tile with one dependent load.
+struct alignas(32) RowTileDesc {
+    int32_t g;      // group
+    int32_t mt0;    // its first row tile
+    int32_t R;      // its row tiles
+    int32_t cnt;    // its rows
+    int32_t goff;   // its first row in expert order (0 for the shared group)
+    int32_t pad[3];
+};
+
 // Arguments of the grouped expert GEMMs.
 struct GroupedArgs {
     int T, d, top_k, n_routed, n_shared, f, fs, G;
@@ -137,7 +149,7 @@ struct GroupedArgs {
     // work queues of the bf16 kernels: row-tile prefix sums, per-XCD
     // row-tile ranges and item counters, column tiles per row tile
     const int32_t *mt_base, *xsplit;
-    const int32_t *rtg;       // group of each row tile
+    const RowTileDesc *rtd;   // group of each row tile
     int32_t *queue;
     int nt_routed, nt_shared;
     const int32_t *perm;      // pair id per expert-ordered row

@@ -37,7 +37,7 @@ __device__ __forceinline__ int find_group(const int32_t *__restrict__ base, int 
 }
 
 struct TileJob {
-    int g, i, j, row0, nrows;
+    int g, i, j, row0, nrows, goff;
     bool shared;
 };
 
@@ -53,6 +53,7 @@ __device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, i
     t.row0 = t.i * bm;
     t.nrows = min(bm, cnt - t.row0);
     t.shared = (t.g == a.n_routed);
+    t.goff = t.shared ? 0 : a.group_off[t.g];
     return t;
 }
 
@@ -108,22 +109,24 @@ __device__ __forceinline__ XcdQueue xcd_queue(const GroupedArgs &a, int x) {
     q.total = q.nr_items + (q.m1 - q.ms) * q.nts;
     return q;
 }
-// Item -> (row tile m, column tile j).  The routed items of a group with
-// rows lo .. lo + r - 1 of the range are items (lo - m0) nt ... + r nt - 1.
+// Item -> (row tile m, column tile j, the group's descriptor).  The routed
+// items of a group with rows lo .. lo + r - 1 of the range are items
+// (lo - m0) nt ... + r nt - 1.
 __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue &q, int item,
-                                           int &m, int &j) {
+                                           int &m, int &j, RowTileDesc &d) {
     int lo, r, local, nt;
     if (item < q.nr_items) {
         nt = q.ntr;
-        const int g = a.rtg[q.m0 + item / nt];
-        lo = max(a.mt_base[g], q.m0);
-        r = min(a.mt_base[g + 1], q.ms) - lo;
+        d = a.rtd[q.m0 + item / nt];
+        lo = max(d.mt0, q.m0);
+        r = min(d.mt0 + d.R, q.ms) - lo;
         local = item - (lo - q.m0) * nt;
     } else {
         nt = q.nts;
         lo = q.ms;
         r = q.m1 - q.ms;
         local = item - q.nr_items;
+        d = a.rtd[q.ms];
     }
     if (item < q.nr_items && r <= kColMajorRows) {
         j = local / r;
@@ -197,9 +200,10 @@ __device__ __forceinline__ int first_item(char *lds, const GroupedArgs &a, int &
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
     return publish_item<P>(lds, a, k, ticket);
 }
-__device__ __forceinline__ void item_tile(const GroupedArgs &a, int item, int &m, int &j) {
+__device__ __forceinline__ void item_tile(const GroupedArgs &a, int item, int &m, int &j,
+                                          RowTileDesc &d) {
     const XcdQueue q = xcd_queue(a, item >> kItemBits);
-    queue_item(a, q, item & ((1 << kItemBits) - 1), m, j);
+    queue_item(a, q, item & ((1 << kItemBits) - 1), m, j, d);
 }
 
 // 4x4 transpose across the four lanes of a quad (lanes 4q .. 4q+3): on
@@ -305,16 +309,18 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
 // work and run at the same speed, so the tiles that stream one weight tile
 // -- adjacent in the queue -- stay close enough for the later ones to find
 // it in L2 (EA read traffic of the V3 gate/up launch 32.0 -> 25.7 GB).
-__device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, int m, int bm) {
+__device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, const RowTileDesc &d, int m,
+                                           int bm) {
     TileJob t;
-    t.g = a.rtg[m];
-    t.i = m - a.mt_base[t.g];
+    t.g = d.g;
+    t.i = m - d.mt0;
     t.j = 0;
-    const int cnt = a.group_cnt[t.g];
-    const int R = a.mt_base[t.g + 1] - a.mt_base[t.g];
+    const int cnt = d.cnt;
+    const int R = d.R;
     const int rpt = min(bm, 32 * ((cnt + 32 * R - 1) / (32 * R)));
     t.row0 = t.i * rpt;
     t.nrows = min(rpt, cnt - t.row0);
+    t.goff = d.goff;
     t.shared = (t.g == a.n_routed);
     return t;
 }
@@ -325,7 +331,7 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
     const int fsum = a.n_shared * a.fs;
     const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
     const int zc0 = tj.j * (P::BN / 2);            // first hidden column of the tile
-    const int goff = tj.shared ? 0 : a.group_off[tj.g];
+    const int goff = tj.goff;
     OperandRows<P> rows;
     rows.abase = (const uint16_t *)a.x;
 #pragma unroll
@@ -369,8 +375,9 @@ __global__ __launch_bounds__(P::NT) void k_gate_up_bf16(const GroupedArgs a) {
     int item = first_item<P>(lds, a, k);
     while (item >= 0) {
         int m, j;
-        item_tile(a, item, m, j);
-        TileJob tj = row_tile(a, m, P::BM);
+        RowTileDesc d;
+        item_tile(a, item, m, j, d);
+        TileJob tj = row_tile(a, d, m, P::BM);
         tj.j = j;
         item = gate_up_body<P>(a, tj, lds, k);
     }
@@ -506,7 +513,7 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
                                          int &k) {
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
-    const int goff = tj.shared ? 0 : a.group_off[tj.g];
+    const int goff = tj.goff;
     // K runs over z, or over (hi, lo) of a split group: the two halves of
     // each 64-wide k-range back to back, so W2 streams once
     const int split = tj.shared ? a.split_s : a.split_r;
@@ -550,8 +557,9 @@ __global__ __launch_bounds__(P::NT) void k_down_bf16(const GroupedArgs a) {
     int item = first_item<P>(lds, a, k);
     while (item >= 0) {
         int m, j;
-        item_tile(a, item, m, j);
-        TileJob tj = row_tile(a, m, P::BM);
+        RowTileDesc d;
+        item_tile(a, item, m, j, d);
+        TileJob tj = row_tile(a, d, m, P::BM);
         tj.j = j;
         item = down_body<P>(a, tj, lds, k);
     }
@@ -568,7 +576,7 @@ __global__ __launch_bounds__(256) void k_gate_up_f32(const GroupedArgs a) {
     for (int tile = tr.first; tile < tr.end; tile += tr.step) {
         const TileJob tj = decode_tile(a, tile, 64);
         const int zc0 = tj.j * 32;
-        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        const int goff = tj.goff;
         const float *arow = nullptr;
         if (lr < tj.nrows) {
             const int tok = tj.shared ? tj.row0 + lr : a.perm[goff + tj.row0 + lr] / a.top_k;
@@ -615,7 +623,7 @@ __global__ __launch_bounds__(256) void k_down_f32(const GroupedArgs a) {
     for (int tile = tr.first; tile < tr.end; tile += tr.step) {
         const TileJob tj = decode_tile(a, tile, 64);
         const int n0 = tj.j * 64;
-        const int goff = tj.shared ? 0 : a.group_off[tj.g];
+        const int goff = tj.goff;
         const int K = tj.shared ? fsum : a.f;
         const float *zin = (const float *)(tj.shared ? a.zs : a.zr);
         const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;

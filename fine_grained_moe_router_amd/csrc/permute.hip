@@ -48,7 +48,7 @@ FwdLayout fwd_layout(const moe_config &c) {
     const TileShape ts = tile_shape(c);
     L.max_row_tiles = (int)(P / ts.bm1) + L.G + (int)(c.T / ts.bm1) + 2;
     L.off_rtg = o;
-    o = align256(o + (size_t)L.max_row_tiles * 4);
+    o = align256(o + (size_t)L.max_row_tiles * sizeof(RowTileDesc));
     L.off_zr = o;
     o = align256(o + P * c.d_ff * eb * (z_split_routed(c) ? 2 : 1));
     L.off_zs = o;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(int N, int n_chunks, int32_t
 __global__ __launch_bounds__(1024) void k_perm_scan(int N, int T, int n_shared, int f, int fsum,
                                                     int d, int split_r, int split_s, TileShape ts,
                                                     int32_t *__restrict__ meta,
-                                                    int32_t *__restrict__ rtg) {
+                                                    RowTileDesc *__restrict__ rtd) {
     __shared__ int32_t cnt[2048], t1[2048], t2[2048], tmp[1024];
     __shared__ int32_t mtb[2048], nt1[2048], nt2[2048], gcost[2048];
     const int G = N + (n_shared > 0 ? 1 : 0);
@@ -239,8 +239,6 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int T, int n_shared, 
     if (threadIdx.x == 0) mtb[G] = totm;
     __syncthreads();
     for (int g = threadIdx.x; g <= G; g += blockDim.x) meta[mi.mt + g] = mtb[g];
-    for (int g = threadIdx.x; g < G; g += blockDim.x)
-        for (int m = mtb[g]; m < mtb[g + 1]; ++m) rtg[m] = g;
     xcd_splits(G, ts.bm1, cnt, mtb, nt1, gcost, tmp, meta + mi.xs1);
     xcd_splits(G, ts.bm1, cnt, mtb, nt2, gcost, tmp, meta + mi.xs2);
     // row offsets of the routed groups (the shared group reads rows 0..T-1)
@@ -248,9 +246,18 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int T, int n_shared, 
     __syncthreads();
     block_excl_scan(cnt, N, tmp);
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
-        meta[mi.group_off + g] = (g < N) ? cnt[g] : 0;
+        const int goff = (g < N) ? cnt[g] : 0;
+        meta[mi.group_off + g] = goff;
         meta[mi.tile1 + g] = t1[g];
         meta[mi.tile2 + g] = t2[g];
+        RowTileDesc dsc;
+        dsc.g = g;
+        dsc.mt0 = mtb[g];
+        dsc.R = mtb[g + 1] - mtb[g];
+        dsc.cnt = meta[mi.group_cnt + g];  // this thread's own earlier store
+        dsc.goff = goff;
+        dsc.pad[0] = dsc.pad[1] = dsc.pad[2] = 0;
+        for (int m = mtb[g]; m < mtb[g + 1]; ++m) rtd[m] = dsc;
     }
     if (threadIdx.x == 0) {
         meta[mi.tile1 + G] = tot1;
@@ -296,7 +303,7 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
                        meta + mi.group_cnt);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, c.T, c.n_shared, c.d_ff,
                        c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
-                       z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (int32_t *)(ws + L.off_rtg));
+                       z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (RowTileDesc *)(ws + L.off_rtg));
     hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
                        L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
                        (float *)(ws + L.off_gsort));

@@ -190,7 +190,7 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     a.group_off = meta + mi.group_off;
     a.group_cnt = meta + mi.group_cnt;
     a.mt_base = meta + mi.mt;
-    a.rtd = (const RowTileDesc *)(ws + L.off_rtg);
+    a.rtd = (const RowTileDesc *)(ws + L.off_rtd);
     a.nt_routed = a.nt_shared = 1;
     a.perm = (const int32_t *)(ws + L.off_perm);
     a.gsort = (const float *)(ws + L.off_gsort);

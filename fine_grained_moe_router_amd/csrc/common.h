@@ -85,7 +85,7 @@ struct FwdLayout {
     size_t off_meta;    // int32 meta block (see MetaIdx)
     size_t off_perm;    // int32 [T*K']: pair id at each expert-ordered row
     size_t off_gsort;   // fp32 [T*K']: gate of each expert-ordered row
-    size_t off_rtg;     // RowTileDesc [max_row_tiles]: the group of each 256-row tile
+    size_t off_rtd;     // RowTileDesc [max_row_tiles]: the group record of each row tile
     int max_row_tiles;  // bound on the row tiles of all groups
     size_t off_zr;      // [T*K'][d_ff] dtype: routed hidden activations
     size_t off_zs;      // [T][K_s*d_ff_shared] dtype: shared hidden activations

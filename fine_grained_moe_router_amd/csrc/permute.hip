@@ -47,7 +47,7 @@ FwdLayout fwd_layout(const moe_config &c) {
     // shared group's T / bm1 + 1
     const TileShape ts = tile_shape(c);
     L.max_row_tiles = (int)(P / ts.bm1) + L.G + (int)(c.T / ts.bm1) + 2;
-    L.off_rtg = o;
+    L.off_rtd = o;
     o = align256(o + (size_t)L.max_row_tiles * sizeof(RowTileDesc));
     L.off_zr = o;
     o = align256(o + P * c.d_ff * eb * (z_split_routed(c) ? 2 : 1));
@@ -303,7 +303,7 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
                        meta + mi.group_cnt);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, c.T, c.n_shared, c.d_ff,
                        c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
-                       z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (RowTileDesc *)(ws + L.off_rtg));
+                       z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (RowTileDesc *)(ws + L.off_rtd));
     hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
                        L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
                        (float *)(ws + L.off_gsort));

@@ -251,6 +251,15 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
     }
     constexpr int SUB = P::BK / 16;          // MFMA k-substeps per k-tile
     constexpr int GROUPS = P::FM;            // MFMA groups (one fragment row each) per substep
+    // Fragment rows start at multiples of 32, so the swizzled slot of this
+    // lane's row (lane & 31 of the fragment) and chunk 2s + lane / 32 is the
+    // same in every fragment: one byte offset per substep, loop-invariant.
+    uint32_t lofs[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+        const int r = lane & 31;
+        lofs[s] = (uint32_t)(r * P::CHUNKS + P::slot(r, 2 * s + (lane >> 5))) * 16u;
+    }
     constexpr int SLOTS = SUB * GROUPS;
     constexpr int LOADS = P::A_LD + P::B_LD;
     for (int kt = 0; kt < nk; ++kt) {
@@ -263,20 +272,21 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
         const size_t kbo = b_koff(min(kt + LB, nk - 1));
         const int sa_next = (kt + 1) % P::A_STAGES;
         const int sb_next = (kt + LB) % P::B_STAGES;
-        const u32x4 *Ab = (const u32x4 *)(a_lds + (kt % P::A_STAGES) * P::A_STAGE);
-        const u32x4 *Bb = (const u32x4 *)(b_lds + (kt % P::B_STAGES) * P::B_STAGE);
+        const char *Ab = a_lds + (kt % P::A_STAGES) * P::A_STAGE;
+        const char *Bb = b_lds + (kt % P::B_STAGES) * P::B_STAGE;
         bf16x8 a[2][NA], b[2][P::FN];
         auto frag_load = [&](int s, bf16x8 (&av)[NA], bf16x8 (&bv)[P::FN]) {
-            const int ch = 2 * s + (lane >> 5);
+            const char *As = Ab + lofs[s];
+            const char *Bs = Bb + lofs[s];
 #pragma unroll
             for (int j = 0; j < P::FN; ++j) {
-                const int row = P::template b_row<SPLIT>(wn, j) + (lane & 31);
-                bv[j] = __builtin_bit_cast(bf16x8, Bb[row * P::CHUNKS + P::slot(row, ch)]);
+                const int row0 = P::template b_row<SPLIT>(wn, j);   // a multiple of 32
+                bv[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Bs + row0 * P::CHUNKS * 16));
             }
 #pragma unroll
             for (int i = 0; i < NF; ++i) {
-                const int row = P::a_row(wm, i) + (lane & 31);
-                av[i] = __builtin_bit_cast(bf16x8, Ab[row * P::CHUNKS + P::slot(row, ch)]);
+                const int row0 = P::a_row(wm, i);
+                av[i] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(As + row0 * P::CHUNKS * 16));
             }
         };
         frag_load(0, a[0], b[0]);

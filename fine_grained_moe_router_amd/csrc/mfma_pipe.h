@@ -36,6 +36,8 @@
 // hold a valid row -- the work of a partial tile scales with ceil(n / 64).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -160,7 +162,7 @@ __device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byt
 // ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several matrices
 // side by side along K, possibly repeated).  AFF: both operands are affine
 // (rows.aoff[0], rows.astep; rows.boff[0], rows.bstep).
-template <class P, bool SPLIT, int NF, bool AFF = false>
+template <class P, bool SPLIT, int NF, bool AFF = false, bool PEEL = true>
 __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &rows, int K,
                                              int bsplit, int bmod, size_t bstride, int a_half,
                                              f32x16 (&acc)[NF > 0 ? NF : 1][P::FN]) {
@@ -262,12 +264,17 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
     }
     constexpr int SLOTS = SUB * GROUPS;
     constexpr int LOADS = P::A_LD + P::B_LD;
-    for (int kt = 0; kt < nk; ++kt) {
+    // One k-tile.  more_a: A(kt+1) exists (kt + 1 < nk); more_b: B(kt+2)
+    // exists.  Passed as std::true_type / std::false_type they are
+    // compile-time constants (PEEL: the main loop then carries no per-load
+    // branches and no choice of wait); passed as bool they are tested per
+    // k-tile.
+    auto k_tile = [&](int kt, auto more_a_c, auto more_b_c) {
+        const bool more_a = more_a_c, more_b = more_b_c;
         // A(kt) and B(kt) have landed (this thread's share) ...
-        if (kt + 1 < nk) wait_vmcnt<P::B_LD>();
+        if (more_a) wait_vmcnt<P::B_LD>();
         else wait_vmcnt<0>();
         lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
-        const bool more_a = kt + 1 < nk, more_b = kt + LB < nk;
         const int ka = min(kt + 1, nk - 1);
         const size_t kbo = b_koff(min(kt + LB, nk - 1));
         const int sa_next = (kt + 1) % P::A_STAGES;
@@ -316,6 +323,16 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+    if constexpr (PEEL) {
+        using yes = std::true_type;
+        using no = std::false_type;
+        int kt = 0;
+        for (; kt + LB < nk; ++kt) k_tile(kt, yes{}, yes{});
+        if (kt + 1 < nk) k_tile(kt++, yes{}, no{});   // kt = nk - 2: B(nk) does not exist
+        if (kt < nk) k_tile(kt, no{}, no{});          // the last k-tile
+    } else {
+        for (int kt = 0; kt < nk; ++kt) k_tile(kt, kt + 1 < nk, kt + LB < nk);
     }
     wait_vmcnt<0>();
     lds_barrier();     // every wave done with the stages before the LDS is reused

@@ -217,14 +217,15 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
             return ((rows.bmask >> n) & 1) ? bbyte[0] + 2u * (uint32_t)n * rows.bstep : bclamp;
         else return bbyte[n];
     };
-    auto a_load = [&](int n, int kt, int stage) {
+    // stage_off: byte offset of the destination stage within the A (B) area
+    auto a_load = [&](int n, int kt, uint32_t stage_off) {
         if ((rows.amask >> n) & 1)
             load_lds16_at(abase, a_byte(n) + 2u * (uint32_t)a_col(kt),
-                          a_lds + stage * P::A_STAGE + (n * P::NT + wave * 64) * 16);
+                          a_lds + stage_off + (n * P::NT + wave * 64) * 16);
     };
-    auto b_load = [&](int n, size_t koff, int stage) {
+    auto b_load = [&](int n, size_t koff, uint32_t stage_off) {
         load_lds16_at(bbase, b_byte(n) + 2u * (uint32_t)koff,
-                      b_lds + stage * P::B_STAGE + (n * P::NT + wave * 64) * 16);
+                      b_lds + stage_off + (n * P::NT + wave * 64) * 16);
     };
     const int nk = K / P::BK;
 #pragma unroll
@@ -249,7 +250,7 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
         if (s >= nk) break;
         const size_t ko = b_koff(s);
 #pragma unroll
-        for (int n = 0; n < P::B_LD; ++n) b_load(n, ko, s);
+        for (int n = 0; n < P::B_LD; ++n) b_load(n, ko, (uint32_t)s * P::B_STAGE);
     }
     constexpr int SUB = P::BK / 16;          // MFMA k-substeps per k-tile
     constexpr int GROUPS = P::FM;            // MFMA groups (one fragment row each) per substep
@@ -269,6 +270,8 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
     // compile-time constants (PEEL: the main loop then carries no per-load
     // branches and no choice of wait); passed as bool they are tested per
     // k-tile.
+    static_assert((P::A_STAGE & (P::A_STAGE - 1)) == 0, "A stage toggle");
+    uint32_t a_cur = 0, b_cur = 0;   // byte offsets of k-tile kt's A and B stages
     auto k_tile = [&](int kt, auto more_a_c, auto more_b_c) {
         const bool more_a = more_a_c, more_b = more_b_c;
         // A(kt) and B(kt) have landed (this thread's share) ...
@@ -277,10 +280,11 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
         lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
         const int ka = min(kt + 1, nk - 1);
         const size_t kbo = b_koff(min(kt + LB, nk - 1));
-        const int sa_next = (kt + 1) % P::A_STAGES;
-        const int sb_next = (kt + LB) % P::B_STAGES;
-        const char *Ab = a_lds + (kt % P::A_STAGES) * P::A_STAGE;
-        const char *Bb = b_lds + (kt % P::B_STAGES) * P::B_STAGE;
+        // stage of k-tile kt + 1 (A, two stages) and kt + 2 = kt - 1 mod 3 (B)
+        const uint32_t sa_next = a_cur ^ (uint32_t)P::A_STAGE;
+        const uint32_t sb_next = b_cur == 0 ? 2u * P::B_STAGE : b_cur - P::B_STAGE;
+        const char *Ab = a_lds + a_cur;
+        const char *Bb = b_lds + b_cur;
         bf16x8 a[2][NA], b[2][P::FN];
         auto frag_load = [&](int s, bf16x8 (&av)[NA], bf16x8 (&bv)[P::FN]) {
             const char *As = Ab + lofs[s];
@@ -323,6 +327,8 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        a_cur = sa_next;
+        b_cur = b_cur == 2u * P::B_STAGE ? 0u : b_cur + P::B_STAGE;
     };
     if constexpr (PEEL) {
         using yes = std::true_type;

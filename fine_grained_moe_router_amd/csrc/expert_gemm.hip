@@ -253,9 +253,7 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
                                             const OperandRows<P> &rows, int zc0, int zw,
                                             size_t rbase, int &k) {
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
-    // gate/up keeps the per-k-tile tests: peeling its last two k-tiles made
-    // it ~1% slower (while down gained ~1%), measured in an interleaved A/B.
-    pipe_gemm_nf<P, true, NF, false, false>(lds, rows, a.d, 0, 1, 0, 0, acc);
+    pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u) in fp32 (the sigmoid from the
     // hardware exponential and reciprocal, each within about an ulp), rounded

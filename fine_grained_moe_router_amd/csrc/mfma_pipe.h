@@ -162,7 +162,7 @@ __device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byt
 // ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several matrices
 // side by side along K, possibly repeated).  AFF: both operands are affine
 // (rows.aoff[0], rows.astep; rows.boff[0], rows.bstep).
-template <class P, bool SPLIT, int NF, bool AFF = false, bool PEEL = true>
+template <class P, bool SPLIT, int NF, bool AFF = false>
 __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &rows, int K,
                                              int bsplit, int bmod, size_t bstride, int a_half,
                                              f32x16 (&acc)[NF > 0 ? NF : 1][P::FN]) {
@@ -217,14 +217,23 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
             return ((rows.bmask >> n) & 1) ? bbyte[0] + 2u * (uint32_t)n * rows.bstep : bclamp;
         else return bbyte[n];
     };
-    // stage_off: byte offset of the destination stage within the A (B) area
-    auto a_load = [&](int n, int kt, uint32_t stage_off) {
+    // kbyte: the k-tile's byte offset along the rows, taken once per k-tile
+    // through readfirstlane so that it stays one scalar (otherwise the
+    // compiler may turn it into one vector induction variable per load);
+    // stage_off: byte offset of the destination stage within the A (B) area.
+    auto a_kbyte = [&](int kt) -> uint32_t {
+        return __builtin_amdgcn_readfirstlane(2u * (uint32_t)a_col(kt));
+    };
+    auto b_kbyte = [&](size_t koff) -> uint32_t {
+        return __builtin_amdgcn_readfirstlane(2u * (uint32_t)koff);
+    };
+    auto a_load = [&](int n, uint32_t kbyte, uint32_t stage_off) {
         if ((rows.amask >> n) & 1)
-            load_lds16_at(abase, a_byte(n) + 2u * (uint32_t)a_col(kt),
+            load_lds16_at(abase, a_byte(n) + kbyte,
                           a_lds + stage_off + (n * P::NT + wave * 64) * 16);
     };
-    auto b_load = [&](int n, size_t koff, uint32_t stage_off) {
-        load_lds16_at(bbase, b_byte(n) + 2u * (uint32_t)koff,
+    auto b_load = [&](int n, uint32_t kbyte, uint32_t stage_off) {
+        load_lds16_at(bbase, b_byte(n) + kbyte,
                       b_lds + stage_off + (n * P::NT + wave * 64) * 16);
     };
     const int nk = K / P::BK;
@@ -244,11 +253,11 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
     static_assert(P::A_STAGES == 2 && P::B_STAGES == 3, "the waits below assume 2 + 3 stages");
     constexpr int LB = P::B_STAGES - 1;
 #pragma unroll
-    for (int n = 0; n < P::A_LD; ++n) a_load(n, 0, 0);
+    for (int n = 0; n < P::A_LD; ++n) a_load(n, 0u, 0u);
 #pragma unroll
     for (int s = 0; s < LB; ++s) {
         if (s >= nk) break;
-        const size_t ko = b_koff(s);
+        const uint32_t ko = b_kbyte(b_koff(s));
 #pragma unroll
         for (int n = 0; n < P::B_LD; ++n) b_load(n, ko, (uint32_t)s * P::B_STAGE);
     }
@@ -266,20 +275,20 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
     constexpr int SLOTS = SUB * GROUPS;
     constexpr int LOADS = P::A_LD + P::B_LD;
     // One k-tile.  more_a: A(kt+1) exists (kt + 1 < nk); more_b: B(kt+2)
-    // exists.  Passed as std::true_type / std::false_type they are
-    // compile-time constants (PEEL: the main loop then carries no per-load
-    // branches and no choice of wait); passed as bool they are tested per
-    // k-tile.
+    // exists.  Both come in as std::true_type / std::false_type, so the main
+    // loop below (where both hold) carries no per-load branches and no
+    // choice of wait; the last two k-tiles are peeled off.
     static_assert((P::A_STAGE & (P::A_STAGE - 1)) == 0, "A stage toggle");
     uint32_t a_cur = 0, b_cur = 0;   // byte offsets of k-tile kt's A and B stages
     auto k_tile = [&](int kt, auto more_a_c, auto more_b_c) {
-        const bool more_a = more_a_c, more_b = more_b_c;
+        constexpr bool more_a = decltype(more_a_c)::value;
+        constexpr bool more_b = decltype(more_b_c)::value;
         // A(kt) and B(kt) have landed (this thread's share) ...
-        if (more_a) wait_vmcnt<P::B_LD>();
+        if constexpr (more_a) wait_vmcnt<P::B_LD>();
         else wait_vmcnt<0>();
         lds_barrier();           // ... everyone's; the stages of k-tile kt-1 are free
-        const int ka = min(kt + 1, nk - 1);
-        const size_t kbo = b_koff(min(kt + LB, nk - 1));
+        const uint32_t ka = a_kbyte(min(kt + 1, nk - 1));
+        const uint32_t kbo = b_kbyte(b_koff(min(kt + LB, nk - 1)));
         // stage of k-tile kt + 1 (A, two stages) and kt + 2 = kt - 1 mod 3 (B)
         const uint32_t sa_next = a_cur ^ (uint32_t)P::A_STAGE;
         const uint32_t sb_next = b_cur == 0 ? 2u * P::B_STAGE : b_cur - P::B_STAGE;
@@ -319,8 +328,8 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
                 for (int n = 0; n < LOADS; ++n) {
                     if (n * SLOTS / LOADS != s * GROUPS + q) continue;
                     if (n < P::A_LD) {
-                        if (more_a) a_load(n, ka, sa_next);
-                    } else if (more_b) {
+                        if constexpr (more_a) a_load(n, ka, sa_next);
+                    } else if constexpr (more_b) {
                         b_load(n - P::A_LD, kbo, sb_next);
                     }
                 }
@@ -330,16 +339,12 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
         a_cur = sa_next;
         b_cur = b_cur == 2u * P::B_STAGE ? 0u : b_cur + P::B_STAGE;
     };
-    if constexpr (PEEL) {
-        using yes = std::true_type;
-        using no = std::false_type;
-        int kt = 0;
-        for (; kt + LB < nk; ++kt) k_tile(kt, yes{}, yes{});
-        if (kt + 1 < nk) k_tile(kt++, yes{}, no{});   // kt = nk - 2: B(nk) does not exist
-        if (kt < nk) k_tile(kt, no{}, no{});          // the last k-tile
-    } else {
-        for (int kt = 0; kt < nk; ++kt) k_tile(kt, kt + 1 < nk, kt + LB < nk);
-    }
+    using yes = std::true_type;
+    using no = std::false_type;
+    int kt = 0;
+    for (; kt + LB < nk; ++kt) k_tile(kt, yes{}, yes{});
+    if (kt + 1 < nk) k_tile(kt++, yes{}, no{});   // kt = nk - 2: B(nk) does not exist
+    if (kt < nk) k_tile(kt, no{}, no{});          // the last k-tile
     wait_vmcnt<0>();
     lds_barrier();     // every wave done with the stages before the LDS is reused
 }

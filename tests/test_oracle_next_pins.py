@@ -254,3 +254,53 @@ def test_bias_update_closed_loop_reduces_skew():
     _, skew1 = load(b, 100)
     assert skew0 > 2.0
     assert skew1 < 0.6 * skew0, (skew0, skew1)
+
+
+def _runs(runs, dtype=np.int64):
+    return np.concatenate([np.full(n, v, dtype) for n, v in runs])
+
+
+@pytest.mark.parametrize("case", [c["name"] for c in golden("bias_update_examples.json")["cases"]])
+def test_bias_update_step_size_worked_examples(case):
+    """The step size of the update, pinned by hand-worked numbers of the
+    pages' examples (tests/golden/bias_update_examples.json): the V4 book's
+    256K-token sequence over 384 experts with top-9 (a hot expert at 36000
+    selections moves by -15/128 alpha, the others at 5400 by +3/1280 alpha)
+    and the DeepSeekMoE notes' worked routing ([-1/2, 1/6, 1/6, 1/6] alpha).
+    The share fbar_i is selections per token (sum_i fbar_i = K'); a reading
+    with the notes' f_i = N' c_i / (K' T) against a target of 1 moves the
+    hot expert by -5 alpha and fails here."""
+    from fractions import Fraction
+    g = next(c for c in golden("bias_update_examples.json")["cases"] if c["name"] == case)
+    N, K, T, alpha = g["n_routed"], g["top_k"], g["n_tok"], g["alpha"]
+    cnt = _runs(g["counts_runs"], np.int32)
+    assert len(cnt) == N
+    b0 = np.full(N, g["bias_in"], np.float32)
+    got = O.bias_update(cnt, T, K, alpha, b0)
+    delta = [Fraction(v) for n, v in g["expected_delta_runs_over_alpha"] for _ in range(n)]
+    want = np.array([float(g["bias_in"]) + alpha * float(d) for d in delta], np.float64)
+    # one rounding of the exact value to fp32 (the oracle works in double)
+    np.testing.assert_allclose(got.astype(np.float64), want, rtol=2 ** -23, atol=0)
+    # the update conserves sum_i b_i when sum_i c_i = K' T (the notes' example)
+    if int(cnt.sum()) == K * T:
+        assert abs(float(np.sum(got.astype(np.float64) - b0))) < 1e-7
+
+
+def test_node_limit_statistics_of_the_v4_book_exercise():
+    """V4 book ch. 02 sec. 4 exercise: 384 experts on 32 nodes of 12, top-9,
+    at most M = 4 nodes per token.  With independent random logits the
+    unrestricted top-9 lies within 4 nodes for far fewer than 1% of tokens,
+    and the limit replaces a large share of the chosen experts (the page:
+    possibly 30% or more).  A limit that is not applied replaces nothing;
+    one applied to the wrong groups keeps more than 4 nodes."""
+    T, N, K, G, M = 4000, 384, 9, 32, 4
+    lg = rand_logits(T, N, 21)
+    plain = O.route(lg, N, K, "sigmoid", True)[0]
+    lim = O.route(lg, N, K, "sigmoid", True, n_groups=G, topk_groups=M)[0]
+    nodes = lim // (N // G)
+    assert max(len(set(r)) for r in nodes) <= M
+    same = np.mean([set(a) == set(b) for a, b in zip(plain, lim)])
+    replaced = np.mean([len(set(a) - set(b)) for a, b in zip(plain, lim)]) / K
+    within4 = np.mean([len(set(r // (N // G))) <= M for r in plain])
+    assert within4 < 0.01 and same < 0.01, (within4, same)
+    assert replaced > 0.30, replaced

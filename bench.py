@@ -20,6 +20,10 @@ workload.  Other modes:
     --extras            one JSON line timing node-limited routing, the
                         in-sequence and device-level statistics and the
                         bias update on the workload's inputs.
+    --calibrate         one JSON line timing bf16 GEMMs of the layer's
+                        expert-GEMM FLOP counts through the vendor library
+                        (torch.matmul / torch.bmm), the attainable-rate
+                        reference of the GPU the layer runs on.
 """
 from __future__ import annotations
 
@@ -42,6 +46,14 @@ COPY_BYTES = 1 << 30           # calibration copy: reads COPY_BYTES/2, writes CO
 
 # Dominant kernel per stage name, with the symbol rocprofv3 reports for it.
 KERNEL_OF_STAGE = {"gate_up": "k_gate_up_bf16", "down": "k_down_bf16"}
+
+# Which roof binds each workload's expert GEMMs, from its arithmetic
+# intensity against MI355X's ridge (2.5 PF / 8 TB/s = 312 FLOP per byte):
+# about 384 rows per expert weight (mid) and 256 (V3 prefill, at the ridge)
+# are compute-bound, 192 rows (V4 skew, Zipf-hot and -cold experts), 21 rows
+# (V4 hash, K' = 1) and 2 rows (V3 decode) are bound by streaming weights.
+BOUND = {"mid": "mfma", "v3_prefill": "mfma", "v3_decode": "hbm", "v4_skew": "hbm",
+         "v4_hash": "hbm"}
 
 
 # Sources that decide what the grouped GEMM kernels do (their code, their
@@ -105,7 +117,22 @@ def parse_args(argv=None):
     ap.add_argument("--extras", action="store_true",
                     help="time the entry points beyond the layer step (node-limited routing, "
                          "in-sequence and device-level statistics, bias update) instead")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time dense and batched bf16 GEMMs of the layer's expert-GEMM FLOP "
+                         "counts through torch.matmul / torch.bmm (hipBLASLt), as the "
+                         "attainable-rate reference of this GPU")
     return ap.parse_args(argv)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class Layer:
@@ -212,6 +239,7 @@ def cpu_baseline(layer, target_s: float):
     n = int(max(probe, min(cfg.T, probe * target_s / max(dt, 1e-3))))
     dt2 = run(n) if n > probe else dt
     return {"value": n / dt2, "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"router logits, routing and layer output of the first {n} of {cfg.T} "
                       f"tokens ({cfg.name}), double-precision C oracle, {dt2:.1f} s wall"}
 
@@ -379,6 +407,39 @@ def extras(cfg):
     return 0
 
 
+def calibrate(reps: int):
+    """One JSON line: TFLOP/s of bf16 GEMMs through the vendor library
+    (torch.matmul / torch.bmm -> hipBLASLt) on random normal operands, with
+    the FLOP counts of the V3 prefill layer's two expert contractions
+    (73,728 rows: 65,536 routed pairs and 8,192 shared rows; d = 7168,
+    d_ff = 2048): dense, and batched as 256 experts of 288 rows each (the
+    same rows spread evenly).  Every operand is contiguous, K-contiguous on
+    the left, N-contiguous on the right."""
+    import torch
+    torch.manual_seed(0)
+    rows, d, f, E = 73728, 7168, 2048, 256
+    shapes = {"dense_gate_up": ((rows, d), (d, 2 * f)), "dense_down": ((rows, f), (f, d)),
+              "grouped_gate_up": ((E, rows // E, d), (E, d, 2 * f)),
+              "grouped_down": ((E, rows // E, f), (E, f, d))}
+    res = {}
+    for name, (sa, sb) in shapes.items():
+        a = torch.randn(sa, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(sb, device="cuda", dtype=torch.bfloat16) * (sa[-1] ** -0.5)
+        fn = (lambda: torch.matmul(a, b)) if len(sa) == 2 else (lambda: torch.bmm(a, b))
+        ms = time_calls(fn, reps=max(reps, 10))
+        flop = 2.0 * a.numel() * sb[-1]
+        res[name] = {"a": list(sa), "b": list(sb), "ms": ms, "tflop": flop / 1e12,
+                     "tflops": flop / (ms * 1e-3) / 1e12,
+                     "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        print(f"[calibrate] {name}: {ms:.3f} ms, {res[name]['tflops']:.0f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del a, b
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "calibrate", "library": "torch.matmul/torch.bmm (hipBLASLt)",
+                      "dtype": "bf16", "reps": max(reps, 10), "gemms": res}))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -402,6 +463,8 @@ def main(argv=None):
     B.lib()   # fails loudly if the HIP library is not built
     if args.extras:
         return extras(cfg)
+    if args.calibrate:
+        return calibrate(args.steps)
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     layer = Layer(cfg)
     torch.cuda.synchronize()
@@ -440,17 +503,24 @@ def main(argv=None):
     stage_ms = {k: (v["ms"] / v["launches"] if v["launches"] else 0.0) for k, v in stages.items()}
     dominant = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     dom_s = stage_ms[dominant] / 1000.0
-    if cfg.dtype == "bf16" and cfg.T >= 1024:
-        achieved = gf[dominant] / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    # both roofs for the dominant kernel: algorithmic FLOPs and algorithmic
+    # bytes of one launch over its average launch time
+    tflops = gf[dominant] / dom_s / 1e12
+    gbs = acc.gemm_bytes(cfg, touched)[dominant] / dom_s / 1e9
+    peak_fl = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    bound = BOUND.get(cfg.name, "mfma" if cfg.T >= 1024 else "hbm")
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak_fl, "unit": "TFLOP/s"}
     else:
-        gb = acc.gemm_bytes(cfg, touched)[dominant]
-        achieved = gb / dom_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = read_traffic(cfg.name, dominant)
     roof["kernel"] = KERNEL_OF_STAGE[dominant]
     roof["avg_launch_ms"] = stage_ms[dominant]
+    roof["mfma_frac"] = tflops / peak_fl
+    roof["hbm_frac"] = gbs / PEAK_HBM_GBS
+    roof["layer_mfma_frac"] = fl["total"] / (ms / 1000.0) / 1e12 / peak_fl
+    roof["layer_hbm_frac"] = by["total"] / (ms / 1000.0) / 1e9 / PEAK_HBM_GBS
 
     out = {
         "metric": "MoE-layer tokens/sec on 1 MI355X (V3 shape, T=8192); % MFMA / HBM roofline",

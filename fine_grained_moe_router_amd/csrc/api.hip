@@ -72,21 +72,27 @@ int validate(const moe_config *c) {
     return MOE_OK;
 }
 
-// Route workspace: [T][N'] fp32 logits (used unless the caller passes its
-// own logits buffer), then [splits][T][N'] fp32 partial sums of a split
-// router GEMM.
+// Route workspace (learned routing): the select blocks' expert histograms,
+// int32 [select_blocks][N'], then, when the router GEMM runs, its output,
+// [splits][T][N'] fp32 -- the logits themselves when it does not split d
+// (unless the caller asked for them in its own buffer), else one partial
+// sum per split, which the select kernel adds up as it reads them.
 size_t route_logits_bytes(const moe_config &c) {
     return ((size_t)c.T * c.n_routed * sizeof(float) + 255) & ~(size_t)255;
 }
+size_t route_hist_bytes(const moe_config &c) {
+    return ((size_t)select_blocks(c) * c.n_routed * sizeof(int32_t) + 255) & ~(size_t)255;
+}
 size_t route_ws(const moe_config &c) {
     if (c.scoring == MOE_ROUTE_HASH) return 0;
-    const int z = router_splits(c);
-    return route_logits_bytes(c) * (z > 1 ? 1 + z : 1);
+    const size_t gemm = (c.flags & MOE_LOGITS_IN) ? 0 : route_logits_bytes(c) * router_splits(c);
+    return route_hist_bytes(c) + gemm;
 }
 
+// p_partial: one row of score sums per select block, then the batch's sums.
 size_t pstat_bytes(const moe_config &c) {
     if (c.scoring == MOE_ROUTE_HASH) return 0;
-    return (size_t)select_blocks(c) * c.n_routed * sizeof(double);
+    return (size_t)(select_blocks(c) + 1) * c.n_routed * sizeof(double);
 }
 
 }  // namespace
@@ -126,29 +132,39 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const fl
             return hip_fail(e);
         return MOE_OK;
     }
-    float *lg = logits;
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    const float *src = logits;   // what the select kernel reads
+    int splits = 1;
+    float *lg_out = nullptr;     // where the select kernel writes the summed logits
+    int32_t *hist_part = (int32_t *)workspace;
     if (c.flags & MOE_LOGITS_IN) {
         if (!logits) return MOE_ERR_INVALID_ARG;
+        if (ws_bytes < route_ws(c)) return MOE_ERR_WORKSPACE;
     } else {
         if (!x || !w_gate) return MOE_ERR_INVALID_ARG;
         if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_UNSUPPORTED;
+        // the router GEMM addresses W_g rows with 32-bit byte offsets
+        if ((long long)c.n_routed * c.d_model >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
         if (c.flags & MOE_LOGITS_OUT) {
             if (!logits) return MOE_ERR_INVALID_ARG;
         } else if (logits) {
             return MOE_ERR_INVALID_ARG;
         }
-        if (!workspace) return MOE_ERR_INVALID_ARG;
         if (ws_bytes < route_ws(c)) return MOE_ERR_WORKSPACE;
-        if (!(c.flags & MOE_LOGITS_OUT)) lg = (float *)workspace;
-        float *part = (float *)((char *)workspace + route_logits_bytes(c));
+        splits = router_splits(c);
+        float *gemm_out = (float *)((char *)workspace + route_hist_bytes(c));
+        if (splits == 1 && (c.flags & MOE_LOGITS_OUT)) gemm_out = logits;
+        else if (c.flags & MOE_LOGITS_OUT) lg_out = logits;
+        src = gemm_out;
         StageScope sc(MOE_STAGE_ROUTER_GEMM, s);
-        if ((e = launch_router_logits(c, x, w_gate, lg, part, s)) != hipSuccess)
+        if ((e = launch_router_logits(c, x, w_gate, gemm_out, route_logits_bytes(c) / sizeof(float),
+                                      s)) != hipSuccess)
             return hip_fail(e);
     }
     StageScope sc(MOE_STAGE_SELECT, s);
-    if ((e = launch_fill_i32(expert_counts, c.n_routed, 0, s)) != hipSuccess) return hip_fail(e);
-    if ((e = launch_select(c, lg, logit_offset, bias, topk_idx, topk_w, expert_counts,
-                           (double *)p_partial, s)) != hipSuccess)
+    if ((e = launch_select(c, src, splits, route_logits_bytes(c) / sizeof(float), lg_out,
+                           logit_offset, bias, topk_idx, topk_w, expert_counts,
+                           (double *)p_partial, hist_part, s)) != hipSuccess)
         return hip_fail(e);
     return MOE_OK;
 }
@@ -235,8 +251,9 @@ int moe_balance_stats(const moe_config *cfg, const int32_t *expert_counts, const
     if ((P || loss) && (!p_partial || c.scoring == MOE_ROUTE_HASH)) return MOE_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     StageScope sc(MOE_STAGE_STATS, s);
-    hipError_t e = launch_balance_stats(c, expert_counts, (P || loss) ? (const double *)p_partial : nullptr,
-                                        select_blocks(c), alpha1, f, P, loss, s);
+    const double *p_sum =
+        (P || loss) ? (const double *)p_partial + (size_t)select_blocks(c) * c.n_routed : nullptr;
+    hipError_t e = launch_balance_stats(c, expert_counts, p_sum, alpha1, f, P, loss, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -162,8 +162,10 @@ struct GroupedArgs {
 
 // ---- launchers (each returns hipSuccess or the launch error) ---------------
 int router_splits(const moe_config &c);   // K splits of the router GEMM
-hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
-                                float *logits, float *part, hipStream_t s);
+// Writes x W_g^T to out (one split), or split z's partial sum to
+// out + z * stride (floats) for z < router_splits(c).
+hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg, float *out,
+                                size_t stride, hipStream_t s);
 hipError_t launch_seq_stats(const moe_config &c, const float *logits, const float *offset,
                             const int32_t *idx, const int32_t *seg_off, int n_seg, float beta,
                             float *scores, float *f_seq, float *p_seq, float *loss,
@@ -173,15 +175,21 @@ hipError_t launch_device_stats(const moe_config &c, const float *f, const float 
                                hipStream_t s);
 hipError_t launch_bias_update(const moe_config &c, const int32_t *counts, long long n_tok,
                               float alpha, float *bias, hipStream_t s);
-hipError_t launch_select(const moe_config &c, const float *logits, const float *offset,
-                         const float *bias, int32_t *idx, float *w, int32_t *counts,
-                         double *p_partial, hipStream_t s);
+// logits: [T][N'] fp32, or `splits` partial sums stride floats apart
+// (added in split order); lg_out: where to write the summed raw logits, or
+// NULL.  hist_part: int32 [select_blocks][N'] scratch; p_partial:
+// [select_blocks + 1][N'] doubles or NULL (the last row receives the
+// batch's score sums); counts: [N'] out.
+hipError_t launch_select(const moe_config &c, const float *logits, int splits, size_t stride,
+                         float *lg_out, const float *offset, const float *bias, int32_t *idx,
+                         float *w, int32_t *counts, double *p_partial, int32_t *hist_part,
+                         hipStream_t s);
 hipError_t launch_hash_route(const moe_config &c, const uint32_t *tid, int32_t *idx,
                              float *w, int32_t *counts, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
-hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts,
-                                const double *p_partial, int n_blocks, float alpha1,
-                                float *f, float *P, float *loss, hipStream_t s);
+// p_sum: [N'] score sums of the batch (row select_blocks of p_partial) or NULL
+hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts, const double *p_sum,
+                                float alpha1, float *f, float *P, float *loss, hipStream_t s);
 int select_blocks(const moe_config &c);   // blocks of the select kernel
 
 // Whether a group's hidden activation z is stored as two bf16 planes

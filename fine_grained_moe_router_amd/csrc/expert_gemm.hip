@@ -140,21 +140,28 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
 
 // Tickets.  Right after the K loop of a tile (and once before the first),
 // thread 0 takes a ticket from the counter of queue (x + k) % 8 (x: the
-// block's XCD; k: thread 0's state, 0 while the XCD's own range lasts).  A
-// ticket past that queue's end moves it on to the next queue -- work
-// stealing once the XCD's own range is drained -- until it holds an item or
-// every queue is drained.  Taking the ticket only when the block is free
-// (rather than one tile ahead) makes the order in which items start follow
-// the queue order, which keeps consecutive items close in time (EA read
-// traffic of the V3 gate/up launch 33.4 -> 31.1 GB).  The ticket's atomic
-// is issued right after the K loop and its result first used after the
-// epilogue's stores, so its latency hides behind them.  The item (queue <<
-// 24 | index, or -1) reaches the other threads through one LDS word in the
-// last B stage, after the down projection's row info (tile_info_offset):
-// after the K loop no wave reads that stage (the epilogues stage their
-// tiles in the others), and the next tile first writes it after the top
-// barrier of its first k-tile, which every wave reaches only after it has
-// read the word.
+// block's XCD; k: how many queues the block has moved past its own, 0 while
+// the XCD's own range lasts).  A ticket past that queue's end moves it on to
+// the next queue -- work stealing once the XCD's own range is drained --
+// until it holds an item or every queue is drained.  Taking the ticket only
+// when the block is free (rather than one tile ahead) makes the order in
+// which items start follow the queue order, which keeps consecutive items
+// close in time (EA read traffic of the V3 gate/up launch 33.4 -> 31.1 GB).
+// The ticket's atomic is issued right after the K loop and its result first
+// used after the epilogue's stores, so its latency hides behind them.  The
+// item (queue << 24 | index, or -1) reaches the other threads through one
+// LDS word in the last B stage, after the down projection's row info
+// (tile_info_offset): after the K loop no wave reads that stage (the
+// epilogues stage their tiles in the others), and the next tile first writes
+// it after the top barrier of its first k-tile, which every wave reaches
+// only after it has read the word.
+//
+// The stealing state k is never kept per thread: every thread derives it
+// from the item just published (queue_step), so all waves hold the same
+// value and take the same branches.  A version that kept k in a per-thread
+// variable advanced by thread 0 alone, and read it in every thread, faulted
+// once stealing began: the waves took different paths around a barrier and
+// read an LDS word that thread 0 had not written.
 constexpr int kItemBits = 24;
 
 // Row info of a down tile (pair id and gate of each of its rows) and then
@@ -170,14 +177,20 @@ constexpr int tile_info_offset() {
 template <class P>
 constexpr int queue_slot_offset() { return tile_info_offset<P>() + 8 * P::BM; }
 
-// Thread 0: the first ticket of a pull (a counter value; unused once every
-// queue is drained, k == kXcds).
+// Queues moved past the block's own (0..7) to reach a published item; 8
+// once every queue is drained (item -1).  The same in every thread.
+__device__ __forceinline__ int queue_step(int item) {
+    if (item < 0) return kXcds;
+    return ((item >> kItemBits) - (int)(blockIdx.x % kXcds) + kXcds) % kXcds;
+}
+// Thread 0: the first ticket of a pull from queue step k (a counter value;
+// unused once every queue is drained, k == kXcds).
 __device__ __forceinline__ int take_ticket(const GroupedArgs &a, int k) {
     return (k < kXcds) ? atomicAdd(a.queue + (blockIdx.x % kXcds + k) % kXcds, 1) : 0;
 }
 // Thread 0: the item a pull ends with, from its first ticket; a ticket past
 // its queue's end moves on to the next queue with a new ticket.
-__device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int &k, int ticket) {
+__device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int k, int ticket) {
     const int x = blockIdx.x % kXcds;
     while (k < kXcds) {
         const int y = (x + k) % kXcds;
@@ -186,19 +199,19 @@ __device__ __forceinline__ int resolve_ticket(const GroupedArgs &a, int &k, int 
     }
     return -1;
 }
-// Called by every thread with thread 0's first ticket of the pull; returns
-// the item to every thread.
+// Called by every thread with thread 0's first ticket of the pull from
+// queue step k; returns the item to every thread.
 template <class P>
-__device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int &k, int ticket) {
+__device__ __forceinline__ int publish_item(char *lds, const GroupedArgs &a, int k, int ticket) {
     int32_t *slot = (int32_t *)(lds + queue_slot_offset<P>());
     if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
     lds_barrier();
     return __builtin_amdgcn_readfirstlane(*slot);
 }
 template <class P>
-__device__ __forceinline__ int first_item(char *lds, const GroupedArgs &a, int &k) {
-    const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
-    return publish_item<P>(lds, a, k, ticket);
+__device__ __forceinline__ int first_item(char *lds, const GroupedArgs &a) {
+    const int ticket = threadIdx.x == 0 ? take_ticket(a, 0) : 0;
+    return publish_item<P>(lds, a, 0, ticket);
 }
 __device__ __forceinline__ void item_tile(const GroupedArgs &a, int item, int &m, int &j,
                                           RowTileDesc &d) {
@@ -251,7 +264,7 @@ __device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
 template <class P, int NF>
 __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                             const OperandRows<P> &rows, int zc0, int zw,
-                                            size_t rbase, int &k) {
+                                            size_t rbase, int k) {
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
     pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
@@ -327,7 +340,7 @@ __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, const RowTileD
 
 template <class P>
 __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                            int &k) {
+                                            int k) {
     const int fsum = a.n_shared * a.fs;
     const int zw = tj.shared ? fsum : a.f;         // hidden width of the group
     const int zc0 = tj.j * (P::BN / 2);            // first hidden column of the tile
@@ -371,15 +384,14 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
 template <class P>
 __global__ __launch_bounds__(P::NT) void k_gate_up_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
-    int k = 0;
-    int item = first_item<P>(lds, a, k);
+    int item = first_item<P>(lds, a);
     while (item >= 0) {
         int m, j;
         RowTileDesc d;
         item_tile(a, item, m, j, d);
         TileJob tj = row_tile(a, d, m, P::BM);
         tj.j = j;
-        item = gate_up_body<P>(a, tj, lds, k);
+        item = gate_up_body<P>(a, tj, lds, queue_step(item));
     }
 }
 
@@ -401,7 +413,7 @@ __device__ __forceinline__ int stage_offset(int row, int col) {
 template <class P, int NF>
 __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                          const OperandRows<P> &rows, int K, int split, int n0,
-                                         int my_pair, float my_gate, int &k) {
+                                         int my_pair, float my_gate, int k) {
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
     if (tj.shared)
         pipe_gemm_nf<P, false, NF, true>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs,
@@ -510,7 +522,7 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
 
 template <class P>
 __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                         int &k) {
+                                         int k) {
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
     const int goff = tj.goff;
@@ -553,15 +565,14 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
 template <class P>
 __global__ __launch_bounds__(P::NT) void k_down_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
-    int k = 0;
-    int item = first_item<P>(lds, a, k);
+    int item = first_item<P>(lds, a);
     while (item >= 0) {
         int m, j;
         RowTileDesc d;
         item_tile(a, item, m, j, d);
         TileJob tj = row_tile(a, d, m, P::BM);
         tj.j = j;
-        item = down_body<P>(a, tj, lds, k);
+        item = down_body<P>(a, tj, lds, queue_step(item));
     }
 }
 

@@ -23,8 +23,9 @@ namespace moe {
 // (m, n, z) computes tokens m*256.., logits n*256.. over k-tiles
 // [z*kps, (z+1)*kps) of d; a tile spans all 256 experts of a V3-sized
 // router, so x is read once.  With one split the block writes the logits;
-// with more it writes its partial sum to part[z] and k_router_reduce adds
-// them in split order.
+// with more it writes its partial sum to out + z * stride, and the select
+// kernel adds the partials of each logit in split order as it reads them
+// (no separate reduction pass, no logits round trip).
 template <int NF>
 __device__ __forceinline__ void router_tile(char *lds, const OperandRows<PipeTile> &rows, int K, int T,
                                             int N, int m0, int n0, float *__restrict__ out) {
@@ -45,6 +46,7 @@ __device__ __forceinline__ void router_tile(char *lds, const OperandRows<PipeTil
 }
 
 __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int N, int kps,
+                                                              size_t stride,
                                                               const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ wg,
                                                               float *__restrict__ out) {
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int 
     const int m0 = blockIdx.x * P::BM, n0 = blockIdx.y * P::BN;
     const int k0 = blockIdx.z * kps * P::BK;
     const int K = min(d - k0, kps * P::BK);
-    out += (size_t)blockIdx.z * T * N;
+    out += (size_t)blockIdx.z * stride;
     const int nrows = min(P::BM, T - m0);
     // Both operands are affine: token rows m0.. and expert rows n0.. (token
     // rows past T are not fetched; expert rows past N' fetch row N' - 1).
@@ -75,17 +77,6 @@ __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int 
         case 1: return router_tile<1>(lds, rows, K, T, N, m0, n0, out);
         default: return router_tile<0>(lds, rows, K, T, N, m0, n0, out);
     }
-}
-
-// logits = sum of the split partials, added in split order.
-__global__ __launch_bounds__(256) void k_router_reduce(int n, int splits,
-                                                       const float *__restrict__ part,
-                                                       float *__restrict__ logits) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    float v = part[i];
-    for (int z = 1; z < splits; ++z) v += part[(size_t)z * n + i];
-    logits[i] = v;
 }
 
 __global__ __launch_bounds__(256) void k_router_f32(int T, int d, int N, const float *__restrict__ x,
@@ -120,8 +111,8 @@ int router_splits(const moe_config &c) {
     return (nk + kps - 1) / kps;
 }
 
-hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg,
-                                float *logits, float *part, hipStream_t s) {
+hipError_t launch_router_logits(const moe_config &c, const void *x, const void *wg, float *out,
+                                size_t stride, hipStream_t s) {
     const int z = router_splits(c);
     if (c.dtype == MOE_BF16) {
         const int nk = c.d_model / PipeTile::BK;
@@ -129,17 +120,11 @@ hipError_t launch_router_logits(const moe_config &c, const void *x, const void *
         dim3 grid((c.T + PipeTile::BM - 1) / PipeTile::BM,
                   (c.n_routed + PipeTile::BN - 1) / PipeTile::BN, z);
         hipLaunchKernelGGL(k_router_bf16, grid, dim3(PipeTile::NT), 0, s, c.T, c.d_model,
-                           c.n_routed, kps, (const uint16_t *)x, (const uint16_t *)wg,
-                           z > 1 ? part : logits);
-        if (z > 1) {
-            const int n = c.T * c.n_routed;
-            hipLaunchKernelGGL(k_router_reduce, dim3((n + 255) / 256), dim3(256), 0, s, n, z,
-                               part, logits);
-        }
+                           c.n_routed, kps, stride, (const uint16_t *)x, (const uint16_t *)wg, out);
     } else {
         dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64);
         hipLaunchKernelGGL(k_router_f32, grid, dim3(256), 0, s, c.T, c.d_model, c.n_routed,
-                           (const float *)x, (const float *)wg, logits);
+                           (const float *)x, (const float *)wg, out);
     }
     return hipGetLastError();
 }
@@ -149,12 +134,14 @@ hipError_t launch_router_logits(const moe_config &c, const void *x, const void *
 constexpr int kSelWaves = 8;
 constexpr int kMaxTopK = 16;
 
-// One token per wavefront for small batches, four at prefill sizes.  The
-// per-token top-K' rounds are a chain of dependent cross-lane steps whose
-// latency the resident waves hide; fewer, fuller blocks also mean fewer
-// per-block score partials for the balance reduction (V3 prefill: 512 -> 256
-// blocks took that reduction from 33 to 20 us at the same select time).
-int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 4 * kSelWaves : kSelWaves; }
+// One token per wavefront for small batches, two at prefill sizes (512
+// blocks of 8 waves at T = 8192: two blocks fit a CU by registers, so the
+// whole batch is in flight at once).  Each block writes its expert
+// histogram and its partial sums of the scores to a row of its own, and
+// k_route_tail adds the rows in block order: no device-wide atomics on the
+// N' counters (from hundreds of blocks on eight XCDs they serialise on a
+// few cache lines).
+int select_tokens_per_block(const moe_config &c) { return c.T >= 4096 ? 2 * kSelWaves : kSelWaves; }
 
 int select_blocks(const moe_config &c) {
     const int tpb = select_tokens_per_block(c);
@@ -170,17 +157,39 @@ __device__ __forceinline__ double score_pointwise(int scoring, float l) {
     return sqrt(sp);
 }
 
-// Logits (plus the optional offset, an fp32 add) and scores s32 of one token
-// held by one wavefront: lane `lane` owns experts lane + 64 j, j < J.
-// Scores are evaluated in double from the fp32 logit and rounded once.
+// Raw logits of one token held by one wavefront: lane `lane` owns experts
+// lane + 64 j, j < J.  The logit is row[e], or with a split router GEMM the
+// sum of its `splits` partials row[e] + row[stride + e] + ..., added in
+// split order in fp32 (so it is one fixed value whoever reads it).
 template <int J>
-__device__ __forceinline__ void wave_token_scores(int N, int scoring, const float *row,
+__device__ __forceinline__ void wave_token_logits(int N, const float *row, int splits,
+                                                  size_t stride, int lane, float (&raw)[J]) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = lane + 64 * j;
+        raw[j] = (e < N) ? row[e] : -INFINITY;
+    }
+    for (int z = 1; z < splits; ++z) {
+        const float *pz = row + (size_t)z * stride;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lane + 64 * j;
+            if (e < N) raw[j] += pz[e];
+        }
+    }
+}
+
+// Logits plus the optional offset (an fp32 add) and scores s32 of one token
+// held by one wavefront.  Scores are evaluated in double from the fp32 logit
+// and rounded once.
+template <int J>
+__device__ __forceinline__ void wave_token_scores(int N, int scoring, const float (&raw)[J],
                                                   const float *offset, int lane, float (&l)[J],
                                                   float (&s32)[J]) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = lane + 64 * j;
-        float v = (e < N) ? row[e] : -INFINITY;
+        float v = raw[j];
         if (offset && e < N) v = v + offset[e];  // fp32 add
         l[j] = v;
     }
@@ -244,9 +253,10 @@ __device__ __forceinline__ void wave_argmax(float &v, int &idx) {
 template <int J, int SC>
 __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
     int T, int N, int K, int renorm, int tpb, int n_groups, int topk_groups,
-    const float *__restrict__ logits, const float *__restrict__ offset,
+    const float *__restrict__ logits, int splits, size_t stride, float *__restrict__ lg_out,
+    const float *__restrict__ offset,
     const float *__restrict__ bias, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-    int32_t *__restrict__ counts, double *__restrict__ p_partial) {
+    int32_t *__restrict__ hist_part, double *__restrict__ p_partial) {
     __shared__ int32_t hist[J * kWave];
     __shared__ double psum[kSelWaves][J * kWave];
     __shared__ float kbuf[kSelWaves][J * kWave];
@@ -262,8 +272,14 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
     const int t0 = blockIdx.x * tpb;
     const int t1 = min(T, t0 + tpb);
     for (int t = t0 + wave; t < t1; t += kSelWaves) {
-        float l[J], key[J], s32[J];
-        wave_token_scores<J>(N, SC, logits + (size_t)t * N, offset, lane, l, s32);
+        float raw[J], l[J], key[J], s32[J];
+        wave_token_logits<J>(N, logits + (size_t)t * N, splits, stride, lane, raw);
+        if (lg_out) {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (lane + 64 * j < N) lg_out[(size_t)t * N + lane + 64 * j] = raw[j];
+        }
+        wave_token_scores<J>(N, SC, raw, offset, lane, l, s32);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int e = lane + 64 * j;
@@ -346,14 +362,15 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
             }
         }
     }
-    // ---- per-block partial sums of s for P_i, combined in a fixed order
+    // ---- this block's expert histogram and partial sums of s (waves added
+    // in a fixed order), one row each for k_route_tail
     if (p_partial) {
 #pragma unroll
         for (int j = 0; j < J; ++j) psum[wave][lane + 64 * j] = pacc[j];
     }
     __syncthreads();
     for (int e = threadIdx.x; e < N; e += blockDim.x) {
-        if (hist[e]) atomicAdd(&counts[e], hist[e]);
+        hist_part[(size_t)blockIdx.x * N + e] = hist[e];
         if (p_partial) {
             double s = psum[0][e];
             for (int w = 1; w < kSelWaves; ++w) s += psum[w][e];
@@ -362,16 +379,56 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
     }
 }
 
-hipError_t launch_select(const moe_config &c, const float *logits, const float *offset,
-                         const float *bias, int32_t *idx, float *w, int32_t *counts,
-                         double *p_partial, hipStream_t s) {
+// Expert counts and score sums of the batch from the select blocks' rows:
+// block (64 experts) x 16 lanes of rows; lane r adds rows r, r + 16, ... in
+// order, then the 16 lane sums are added in r order (a fixed order, so the
+// score sums do not depend on timing).  The score sums go to row nblk of
+// p_partial, where moe_balance_stats reads them.
+constexpr int kTailRows = 16;
+__global__ __launch_bounds__(kTailRows * kWave) void k_route_tail(int N, int nblk,
+                                                                  const int32_t *__restrict__ hist_part,
+                                                                  double *__restrict__ p_partial,
+                                                                  int32_t *__restrict__ counts) {
+    __shared__ int32_t hs[kTailRows][kWave];
+    __shared__ double ps[kTailRows][kWave];
+    const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const int e = blockIdx.x * kWave + c;
+    int h = 0;
+    double p = 0.0;
+    if (e < N) {
+#pragma unroll 4
+        for (int b = r; b < nblk; b += kTailRows) {
+            h += hist_part[(size_t)b * N + e];
+            if (p_partial) p += p_partial[(size_t)b * N + e];
+        }
+    }
+    hs[r][c] = h;
+    ps[r][c] = p;
+    __syncthreads();
+    if (r == 0 && e < N) {
+        int H = 0;
+        double S = 0.0;
+        for (int q = 0; q < kTailRows; ++q) {
+            H += hs[q][c];
+            S += ps[q][c];
+        }
+        counts[e] = H;
+        if (p_partial) p_partial[(size_t)nblk * N + e] = S;
+    }
+}
+
+hipError_t launch_select(const moe_config &c, const float *logits, int splits, size_t stride,
+                         float *lg_out, const float *offset, const float *bias, int32_t *idx,
+                         float *w, int32_t *counts, double *p_partial, int32_t *hist_part,
+                         hipStream_t s) {
     const int J = (c.n_routed + 63) / 64;
     const int tpb = select_tokens_per_block(c);
     dim3 grid(select_blocks(c)), block(kSelWaves * kWave);
 #define MOE_SEL_SC(JJ, SC)                                                                     \
     hipLaunchKernelGGL((k_select<JJ, SC>), grid, block, 0, s, c.T, c.n_routed, c.top_k,       \
-                       c.renorm, tpb, c.n_groups, c.topk_groups, logits, offset, bias, idx, w, \
-                       counts, p_partial)
+                       c.renorm, tpb, c.n_groups, c.topk_groups, logits, splits, stride,       \
+                       lg_out, offset, bias, idx, w,                                           \
+                       hist_part, p_partial)
 #define MOE_SEL(JJ)                                                                            \
     do {                                                                                       \
         if (c.scoring == MOE_SCORE_SOFTMAX) MOE_SEL_SC(JJ, MOE_SCORE_SOFTMAX);                 \
@@ -386,6 +443,8 @@ hipError_t launch_select(const moe_config &c, const float *logits, const float *
     else MOE_SEL(16);
 #undef MOE_SEL_SC
 #undef MOE_SEL
+    hipLaunchKernelGGL(k_route_tail, dim3((c.n_routed + kWave - 1) / kWave), dim3(kTailRows * kWave),
+                       0, s, c.n_routed, select_blocks(c), hist_part, p_partial, counts);
     return hipGetLastError();
 }
 
@@ -413,8 +472,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_scores(int T, int N, int 
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
     if (t >= T) return;
-    float l[J], s32[J];
-    wave_token_scores<J>(N, scoring, logits + (size_t)t * N, offset, lane, l, s32);
+    float raw[J], l[J], s32[J];
+    wave_token_logits<J>(N, logits + (size_t)t * N, 1, 0, lane, raw);
+    wave_token_scores<J>(N, scoring, raw, offset, lane, l, s32);
 #pragma unroll
     for (int j = 0; j < J; ++j)
         if (lane + 64 * j < N) s32_out[(size_t)t * N + lane + 64 * j] = s32[j];
@@ -612,42 +672,26 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
 
 // ============================================================ balance stats
 
-// f_i = N' c_i / (K' T); P_i = (1/T) sum over blocks of the partial sums (in
-// block order); loss = alpha1 / N' sum_i f_i P_i (double, fixed tree order).
-// One block.  Expert e's per-block partial sums of s are split over G
-// threads (G = 1024 / Np, Np = N rounded up to a power of two): thread
-// (r, e) adds the partials of blocks r, r + G, ..., and the G sums are then
-// added in r order -- a fixed order, so P is reproducible.
+// f_i = N' c_i / (K' T); P_i = (1/T) times the batch's score sum (row
+// p_sum, written by k_route_tail); loss = alpha1 / N' sum_i f_i P_i (double,
+// fixed tree order).  One block, one thread per expert.
 __global__ __launch_bounds__(1024) void k_balance(int T, int N, int K, const int32_t *__restrict__ c,
-                                                  const double *__restrict__ part, int nblk,
-                                                  float alpha1, float *__restrict__ f,
-                                                  float *__restrict__ P, float *__restrict__ loss) {
+                                                  const double *__restrict__ p_sum, float alpha1,
+                                                  float *__restrict__ f, float *__restrict__ P,
+                                                  float *__restrict__ loss) {
     __shared__ double red[1024];
-    int Np = 1;
-    while (Np < N) Np <<= 1;
-    const int G = 1024 / Np;
-    const int e = threadIdx.x % Np, r = threadIdx.x / Np;
-    double s = 0.0;
-    if (part && e < N) {
-#pragma unroll 8
-        for (int b = r; b < nblk; b += G) s += part[(size_t)b * N + e];
-    }
-    red[threadIdx.x] = s;
-    __syncthreads();
+    const int e = threadIdx.x;
     double acc = 0.0;
-    if (r == 0 && e < N) {
+    if (e < N) {
         const double fe = (double)((int64_t)N * c[e]) / (double)((int64_t)K * T);
         f[e] = (float)fe;
-        if (part) {
-            double tot = 0.0;
-            for (int q = 0; q < G; ++q) tot += red[q * Np + e];
-            const double pe = tot / (double)T;
+        if (p_sum) {
+            const double pe = p_sum[e] / (double)T;
             if (P) P[e] = (float)pe;
             acc = fe * pe;
         }
     }
     if (!loss) return;
-    __syncthreads();
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int o = blockDim.x / 2; o > 0; o >>= 1) {
@@ -659,11 +703,10 @@ __global__ __launch_bounds__(1024) void k_balance(int T, int N, int K, const int
         loss[1] = (float)red[0];
     }
 }
-hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts,
-                                const double *p_partial, int n_blocks, float alpha1, float *f,
-                                float *P, float *loss, hipStream_t s) {
+hipError_t launch_balance_stats(const moe_config &c, const int32_t *counts, const double *p_sum,
+                                float alpha1, float *f, float *P, float *loss, hipStream_t s) {
     hipLaunchKernelGGL(k_balance, dim3(1), dim3(1024), 0, s, c.T, c.n_routed, c.top_k, counts,
-                       p_partial, n_blocks, alpha1, f, P, loss);
+                       p_sum, alpha1, f, P, loss);
     return hipGetLastError();
 }
 

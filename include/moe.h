@@ -100,7 +100,9 @@ typedef struct {
 #define MOE_WS_ROUTE 0    /* scratch of moe_route                               */
 #define MOE_WS_FORWARD 1  /* scratch of moe_forward                             */
 #define MOE_WS_PSTAT 2    /* the p_partial buffer moe_route fills for
-                             moe_balance_stats                                  */
+                             moe_balance_stats (its content is internal: score
+                             sums per block of the selection, then the batch's
+                             sums, all double)                                 */
 #define MOE_WS_SEQSTAT 3  /* scratch of moe_seq_balance_stats                   */
 
 /* Bytes of the requested buffer for this config; 0 if the config is invalid
@@ -129,8 +131,9 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which);
  *   topk_w[t][k] = s[idx]  or  s[idx] / sum_k' s[idx_k'] (renorm; double sum
  *           in k order, rounded once)
  *   expert_counts[i] = #{(t, k) : topk_idx[t][k] == i}  (overwritten)
- *   p_partial: per-block partial sums of s used for P_i by
- *           moe_balance_stats (may be NULL; must be NULL under HASH)
+ *   p_partial: partial sums of s (one row per block of the selection)
+ *           and the batch's sums, read by moe_balance_stats for P_i (may be
+ *           NULL; must be NULL under HASH)
  * Arguments
  *   x          [T][d] bf16 or fp32 (cfg->dtype); unused with MOE_LOGITS_IN
  *              or HASH
@@ -143,13 +146,18 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which);
  *   topk_idx   [T][K'] int32 out;  topk_w [T][K'] fp32 out
  *   expert_counts [N'] int32 out
  *   workspace  >= moe_workspace_bytes(cfg, MOE_WS_ROUTE) bytes; required
- *              whenever the router GEMM runs (not with MOE_LOGITS_IN or
- *              HASH): it holds the logits (unless MOE_LOGITS_OUT) and, for
- *              small batches, the partial sums of a K-split GEMM
+ *              for learned routing (not under HASH): it holds the expert
+ *              histograms of the selection's blocks (added in block order,
+ *              so no device-wide atomics), and, when the router GEMM runs,
+ *              its output -- the logits (unless MOE_LOGITS_OUT and an
+ *              unsplit GEMM), or, where d is split to cover the compute
+ *              units, one partial sum per split, which the selection adds in
+ *              split order as it reads them
  * Errors: INVALID_ARG for a NULL required pointer, an out-of-range field,
  * HASH with K' != 1, missing token_ids, or p_partial under HASH;
- * UNSUPPORTED for d or widths not multiples of 64; WORKSPACE when ws_bytes
- * is too small; HIP when a launch fails.
+ * UNSUPPORTED for d or widths not multiples of 64, or N' d >= 2^31 when the
+ * router GEMM runs (it addresses W_g with 32-bit offsets); WORKSPACE when
+ * ws_bytes is too small; HIP when a launch fails.
  */
 int moe_route(const moe_config *cfg, const void *x, const void *w_gate,
               const float *logit_offset, const float *bias,

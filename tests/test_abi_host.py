@@ -106,18 +106,26 @@ def route(L, c, x=P, wg=P, off=None, bias=None, tid=None, logits=None, idx=P, w=
 
 
 def test_route_workspace_holds_split_partials():
-    # The router GEMM splits d so that its 256 x 256 tiles cover the CUs: the
-    # route workspace then holds the logits plus one [T][N'] partial per
-    # split (at most 16 splits of at least 8 k-tiles each).  With d below
-    # 8 k-tiles of 64 it does not split.
+    # The route workspace holds the select blocks' expert histograms (one
+    # int32 row of N' per block, blocks of at least 8 tokens) and, when the
+    # router GEMM runs, its output.  The GEMM splits d so that its 256 x 256
+    # tiles cover the CUs: then it holds one [T][N'] partial per split (at
+    # most 16 splits of at least 8 k-tiles each), which the select kernel
+    # adds up; unsplit, the logits.  With d below 8 k-tiles of 64 it does not
+    # split.  With MOE_LOGITS_IN only the histograms remain.
     for name in ("v3_decode", "v3_prefill"):
-        c = B.make_config(CONFIGS[name])
-        tn = CONFIGS[name].T * CONFIGS[name].n_routed * 4
-        ws = B.workspace_bytes(c, B.WS_ROUTE)
-        assert ws % tn == 0 and 3 * tn <= ws <= 17 * tn, name
+        cfg = CONFIGS[name]
+        tn = cfg.T * cfg.n_routed * 4
+        hist_max = -(-cfg.T // 8) * cfg.n_routed * 4 + 256
+        ws = B.workspace_bytes(B.make_config(cfg), B.WS_ROUTE)
+        assert 2 * tn <= ws <= 16 * tn + hist_max, name
+        ws_in = B.workspace_bytes(B.make_config(cfg, flags=B.LOGITS_IN), B.WS_ROUTE)
+        assert 0 < ws_in <= hist_max and (ws - ws_in) % tn == 0, name
     narrow = CONFIGS["toy_fp32"].with_(dtype="bf16", d_model=256)
     tn = narrow.T * narrow.n_routed * 4
-    assert B.workspace_bytes(B.make_config(narrow), B.WS_ROUTE) == tn
+    ws = B.workspace_bytes(B.make_config(narrow), B.WS_ROUTE)
+    ws_in = B.workspace_bytes(B.make_config(narrow, flags=B.LOGITS_IN), B.WS_ROUTE)
+    assert ws - ws_in == tn
 
 
 def test_route_argument_errors(L):
@@ -135,10 +143,16 @@ def test_route_argument_errors(L):
     cin = cfg_of("v3_decode")
     cin.flags = B.LOGITS_IN
     assert route(L, cin, logits=None) == B.MOE_ERR_INVALID_ARG
+    assert route(L, cin, logits=P, ws=None) == B.MOE_ERR_INVALID_ARG   # histogram rows
+    assert route(L, cin, logits=P, ws_bytes=16) == B.MOE_ERR_WORKSPACE
     cout = cfg_of("v3_decode")
     cout.flags = B.LOGITS_OUT
     assert route(L, cout, logits=None) == B.MOE_ERR_INVALID_ARG
     assert route(L, cout, logits=P, ws=None) == B.MOE_ERR_INVALID_ARG  # split partials need it
+    # the router GEMM addresses W_g with 32-bit byte offsets: N' d < 2^31
+    big = cfg_of("v3_decode", T=8, d_model=1 << 21, n_routed=1024, d_ff=64, n_shared=0)
+    assert L.moe_workspace_bytes(ctypes.byref(big), B.WS_FORWARD) > 0   # the layer itself is valid
+    assert route(L, big) == B.MOE_ERR_UNSUPPORTED
     h = cfg_of("v4_hash")
     assert route(L, h, tid=None) == B.MOE_ERR_INVALID_ARG       # hash needs token ids
     assert route(L, h, tid=P, pstat=P) == B.MOE_ERR_INVALID_ARG  # no P under hash

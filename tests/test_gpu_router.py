@@ -69,3 +69,19 @@ def test_router_logits_match_oracle(name):
     assert (err <= bound).all(), (name, float((err / np.maximum(bound, 1e-30)).max()))
     # and the typical error is far below the worst case
     assert float(np.median(err)) <= 0.05 * float(np.median(bound)) + 1e-7
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_routing_without_logits_out_is_identical(name):
+    """The select kernel adds the router's split partials itself.  Whether
+    or not the caller asks for the summed logits (MOE_LOGITS_OUT), the
+    routing, counts and score partial sums are the same bits."""
+    cfg = CASES[name]
+    inp = make_inputs(cfg, "cuda", experts=False)
+    a = B.route(cfg, x=inp.x, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias,
+                logits_out=True)
+    b = B.route(cfg, x=inp.x, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias,
+                logits_out=False)
+    torch.cuda.synchronize()
+    for k in ("idx", "w", "counts", "pstat"):
+        assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k

@@ -24,7 +24,8 @@ LOGITS_IN, LOGITS_OUT = 1, 2
 WS_ROUTE, WS_FORWARD, WS_PSTAT, WS_SEQSTAT = 0, 1, 2, 3
 STAGES = ("router_gemm", "select", "permute", "gate_up", "down", "combine", "stats")
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_balance_stats",
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_static",
+           "moe_balance_stats",
            "moe_seq_balance_stats", "moe_device_balance_stats", "moe_bias_update",
            "moe_status_string", "moe_profile_enable", "moe_profile_collect")
 
@@ -68,6 +69,8 @@ def lib():
     L.moe_route.restype = i32
     L.moe_forward.argtypes = [cfgp] + [vp] * 9 + [sz, vp]
     L.moe_forward.restype = i32
+    L.moe_forward_static.argtypes = [cfgp] + [vp] * 9
+    L.moe_forward_static.restype = i32
     L.moe_balance_stats.argtypes = [cfgp, vp, vp, f32, vp, vp, vp, vp]
     L.moe_balance_stats.restype = i32
     L.moe_seq_balance_stats.argtypes = [cfgp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
@@ -199,6 +202,34 @@ def forward(cfg: LayerConfig, x, idx, w, w13, w2, w13s=None, w2s=None, h=None, w
     rc = lib().moe_forward(ctypes.byref(c), _p(x), _p(idx), _p(w), _p(w13), _p(w2), _p(w13s),
                            _p(w2s), _p(h), _p(workspace), workspace.numel(), _stream(stream))
     _check(rc, "moe_forward")
+    return h
+
+
+def forward_static(cfg: LayerConfig, x, idx, w, w13, w2, w13s=None, w2s=None, h=None,
+                   stream=None) -> torch.Tensor:
+    """moe_forward_static: moe_forward on the library's own device scratch
+    (no workspace argument; the library allocates nothing).  Returns h."""
+    c = make_config(cfg)
+    T, d, N, K, f = cfg.T, cfg.d_model, cfg.n_routed, cfg.top_k, cfg.d_ff
+    et = _elem(cfg)
+    _need(x, (T, d), et, "x")
+    _need(idx, (T, K), torch.int32, "idx")
+    _need(w, (T, K), torch.float32, "w")
+    _need(w13, (N, 2 * f, d), et, "w13")
+    _need(w2, (N, d, f), et, "w2")
+    if cfg.n_shared > 0:
+        fs = cfg.d_ff_shared
+        _need(w13s, (cfg.n_shared, 2 * fs, d), et, "w13s")
+        _need(w2s, (cfg.n_shared, d, fs), et, "w2s")
+    else:
+        w13s = w2s = None
+    if h is None:
+        h = torch.empty((T, d), dtype=et, device=x.device)
+    else:
+        _need(h, (T, d), et, "h")
+    rc = lib().moe_forward_static(ctypes.byref(c), _p(x), _p(idx), _p(w), _p(w13), _p(w2),
+                                  _p(w13s), _p(w2s), _p(h), _stream(stream))
+    _check(rc, "moe_forward_static")
     return h
 
 

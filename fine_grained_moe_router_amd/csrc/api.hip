@@ -2,6 +2,7 @@
 // validation, workspace layout, and the order of kernel launches.
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -38,6 +39,10 @@ struct StageScope {
         if (idx >= 0) (void)hipEventRecord(g_prof.ev[2 * idx + 1], s);
     }
 };
+
+// The GEMMs move 16-byte chunks of every activation and weight row (rows
+// are multiples of 64 elements), and the combine 16 bytes of x and h.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 // ---- validation ----------------------------------------------------------------
 int validate(const moe_config *c) {
@@ -95,6 +100,56 @@ size_t pstat_bytes(const moe_config &c) {
     return (size_t)(select_blocks(c) + 1) * c.n_routed * sizeof(double);
 }
 
+// ---- library-owned scratch of moe_forward_static -------------------------------
+// For callers that cannot allocate device memory.  Each GPU the library runs
+// on holds its own copy of this array until the process ends.  In host code
+// the name `scratch` is only a host-side stand-in symbol, never a device
+// address: host code uses the per-device address from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = 64ull << 20;   // MOE_STATIC_SCRATCH_BYTES
+static_assert(kStaticScratchBytes == (size_t)MOE_STATIC_SCRATCH_BYTES, "header and library agree");
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// Argument checks shared by moe_forward and moe_forward_static (not the
+// workspace).
+int check_forward_args(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                       const float *topk_w, const void *w13, const void *w2,
+                       const void *w13_shared, const void *w2_shared, const void *h) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    const moe_config &c = *cfg;
+    if (!x || !topk_idx || !topk_w || !w13 || !w2 || !h) return MOE_ERR_INVALID_ARG;
+    if (c.n_shared > 0 && (!w13_shared || !w2_shared)) return MOE_ERR_INVALID_ARG;
+    if (h == x) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) ||
+        (c.n_shared > 0 && (!aligned16(w13_shared) || !aligned16(w2_shared))))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int forward_impl(const moe_config &c, const void *x, const int32_t *topk_idx, const float *topk_w,
+                 const void *w13, const void *w2, const void *w13_shared, const void *w2_shared,
+                 void *h, char *ws, hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -109,10 +164,6 @@ size_t moe_workspace_bytes(const moe_config *cfg, int which) {
         default: return 0;
     }
 }
-
-// The GEMMs move 16-byte chunks of every activation and weight row (rows
-// are multiples of 64 elements), and the combine 16 bytes of x and h.
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const float *logit_offset,
               const float *bias, const uint32_t *token_ids, float *logits, int32_t *topk_idx,
@@ -172,19 +223,39 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_gate, const fl
 int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, const float *topk_w,
                 const void *w13, const void *w2, const void *w13_shared, const void *w2_shared,
                 void *h, void *workspace, size_t ws_bytes, void *stream) {
-    int rc = validate(cfg);
+    int rc = check_forward_args(cfg, x, topk_idx, topk_w, w13, w2, w13_shared, w2_shared, h);
     if (rc) return rc;
-    const moe_config &c = *cfg;
-    if (!x || !topk_idx || !topk_w || !w13 || !w2 || !h || !workspace) return MOE_ERR_INVALID_ARG;
-    if (c.n_shared > 0 && (!w13_shared || !w2_shared)) return MOE_ERR_INVALID_ARG;
-    if (h == x) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) ||
-        (c.n_shared > 0 && (!aligned16(w13_shared) || !aligned16(w2_shared))))
-        return MOE_ERR_UNSUPPORTED;
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < fwd_layout(*cfg).total) return MOE_ERR_WORKSPACE;
+    return forward_impl(*cfg, x, topk_idx, topk_w, w13, w2, w13_shared, w2_shared, h,
+                        (char *)workspace, (hipStream_t)stream);
+}
+
+int moe_forward_static(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                       const float *topk_w, const void *w13, const void *w2,
+                       const void *w13_shared, const void *w2_shared, void *h, void *stream) {
+    int rc = check_forward_args(cfg, x, topk_idx, topk_w, w13, w2, w13_shared, w2_shared, h);
+    if (rc) return rc;
+    if (fwd_layout(*cfg).total > kStaticScratchBytes) return MOE_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if ((rc = static_scratch(&ws)) != MOE_OK) return rc;
+    return forward_impl(*cfg, x, topk_idx, topk_w, w13, w2, w13_shared, w2_shared, h, (char *)ws,
+                        (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of the layer's expert part on a validated config and
+// a workspace of at least fwd_layout(c).total bytes (the caller's, or the
+// library-owned scratch).  The permutation clears the work counters the
+// GEMMs start from, so no workspace content survives from one call into
+// the next.
+int forward_impl(const moe_config &c, const void *x, const int32_t *topk_idx, const float *topk_w,
+                 const void *w13, const void *w2, const void *w13_shared, const void *w2_shared,
+                 void *h, char *ws, hipStream_t s) {
     const FwdLayout L = fwd_layout(c);
-    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    char *ws = (char *)workspace;
     hipError_t e;
     {
         StageScope sc(MOE_STAGE_PERMUTE, s);
@@ -241,6 +312,11 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx, c
     }
     return MOE_OK;
 }
+
+
+}  // namespace
+
+extern "C" {
 
 int moe_balance_stats(const moe_config *cfg, const int32_t *expert_counts, const void *p_partial,
                       float alpha1, float *f, float *P, float *loss, void *stream) {

@@ -199,6 +199,33 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                 void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * moe_forward_static -- moe_forward with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Computes exactly what moe_forward computes (the same kernels), using a
+ * library-owned device array of MOE_STATIC_SCRATCH_BYTES as its workspace.
+ * Each GPU the library runs on holds its own copy of that array until the
+ * process ends (it is part of the library's device code, placed when the
+ * library is loaded on that GPU); its address is looked up once per device
+ * on the first call with that device current.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *  - Configs whose moe_workspace_bytes(cfg, MOE_WS_FORWARD) exceeds
+ *    MOE_STATIC_SCRATCH_BYTES return MOE_ERR_UNSUPPORTED (at the V3 layer
+ *    shape, batches of up to about 150 tokens fit: decode-sized work).
+ *  - Every call on one GPU shares that GPU's array and leaves its contents
+ *    behind; nothing in it needs to start at zero (the call clears what its
+ *    kernels count from).  Calls that overlap on one GPU -- on different
+ *    streams, or from host threads without ordering -- RACE on the array and
+ *    give undefined results: order them on one stream.
+ * Arguments and the other errors as for moe_forward.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64ull << 20)
+int moe_forward_static(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                       const float *topk_w, const void *w13, const void *w2,
+                       const void *w13_shared, const void *w2_shared, void *h, void *stream);
+
+/*
  * moe_balance_stats -- expert-level balance statistics of the DeepSeekMoE
  * notes ("Expert-level balance loss" equations), routed experts only:
  *   f_i = N' c_i / (K' T)          (c = expert_counts)

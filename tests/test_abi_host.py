@@ -239,3 +239,22 @@ def test_device_stats_and_bias_update_argument_errors(L):
     assert u(ctypes.byref(c), None, 8192, al, P, None) == B.MOE_ERR_INVALID_ARG
     assert u(ctypes.byref(c), P, 0, al, P, None) == B.MOE_ERR_INVALID_ARG
     assert u(ctypes.byref(c), P, 8192, al, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_forward_static_refuses_configs_beyond_its_scratch(L):
+    """moe_forward_static runs on a library-owned scratch of
+    MOE_STATIC_SCRATCH_BYTES (64 MiB): a larger forward workspace is refused
+    before anything touches a device; its other argument checks are
+    moe_forward's."""
+    big = cfg_of("v3_prefill")
+    assert B.workspace_bytes(big, B.WS_FORWARD) > 64 << 20
+    args = [ctypes.c_void_p(4096 * (i + 1)) for i in range(8)]
+    assert L.moe_forward_static(ctypes.byref(big), *args, None) == B.MOE_ERR_UNSUPPORTED
+    small = cfg_of("v3_decode")
+    assert B.workspace_bytes(small, B.WS_FORWARD) <= 64 << 20
+    a = list(args)
+    a[0] = None
+    assert L.moe_forward_static(ctypes.byref(small), *a, None) == B.MOE_ERR_INVALID_ARG
+    a = list(args)
+    a[7] = a[0]                                # h aliases x
+    assert L.moe_forward_static(ctypes.byref(small), *a, None) == B.MOE_ERR_INVALID_ARG

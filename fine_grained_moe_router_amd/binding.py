@@ -15,7 +15,11 @@ import torch
 
 from .configs import LayerConfig
 
-LIB_PATH = Path(__file__).resolve().parent / "libmoe.so"
+import os
+
+# The in-tree library, or (MOE_LIB) another build of the same sources, such
+# as the host-sanitised one the CPU sanitizer test makes.
+LIB_PATH = Path(os.environ.get("MOE_LIB", Path(__file__).resolve().parent / "libmoe.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 SCORING = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "hash": 3}

@@ -88,10 +88,18 @@ __device__ __forceinline__ TileRange tile_range(int total) {
 // items left takes them from the other XCDs' queues).  Item order within a
 // group: a routed expert with at most kColMajorRows row tiles in the range
 // lists them row tile fastest -- its row tiles that stream the same weight
-// tile start together -- while a longer group (the shared experts, a
-// heavily loaded expert) lists column tile fastest, so the gang of column
-// tiles on one row tile shares its token rows.
+// tile start together, and its 16 (gate/up) or 28 (down) column tiles take
+// at most one XCD's worth of blocks.  A longer group (the shared experts, a
+// Zipf-hot expert with up to 25 row tiles at the V4 shape) is listed in
+// panels of kPanelRows row tiles x kPanelCols column tiles, 32 items, the
+// blocks of one XCD: a panel's blocks share 4 token-row tiles and 8 weight
+// tiles through the XCD's L2, 12 distinct operand tiles per k-step against
+// 18 for the same 32 items taken column tile fastest (2 row tiles x 16
+// column tiles), and a weight tile is streamed once per 4 row tiles instead
+// of once per row tile.  Interleaved A/B against column-fastest order: V4
+// skew gate/up -4.3%, down -3%; V3 prefill gate/up -0.8%.
 constexpr int kColMajorRows = 4;
+constexpr int kPanelRows = 4, kPanelCols = 8;
 
 struct XcdQueue {
     int m0, ms, m1, ntr, nts, nr_items, total;
@@ -132,9 +140,15 @@ __device__ __forceinline__ void queue_item(const GroupedArgs &a, const XcdQueue 
         j = local / r;
         m = lo + (local - j * r);
     } else {
-        const int i = local / nt;
-        m = lo + i;
-        j = local - i * nt;
+        // panel rb of (up to) kPanelRows row tiles spans all nt column tiles
+        // in blocks of kPanelCols; inside a block the row tile runs fastest
+        const int rb = local / (kPanelRows * nt);
+        const int pr = min(kPanelRows, r - rb * kPanelRows);
+        const int idx = local - rb * kPanelRows * nt;
+        const int cb = idx / (pr * kPanelCols);
+        const int k = idx - cb * pr * kPanelCols;
+        m = lo + rb * kPanelRows + k % pr;
+        j = cb * kPanelCols + k / pr;
     }
 }
 

@@ -380,19 +380,19 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
 }
 
 // Expert counts and score sums of the batch from the select blocks' rows:
-// block (64 experts) x 16 lanes of rows; lane r adds rows r, r + 16, ... in
-// order, then the 16 lane sums are added in r order (a fixed order, so the
-// score sums do not depend on timing).  The score sums go to row nblk of
-// p_partial, where moe_balance_stats reads them.
-constexpr int kTailRows = 16;
-__global__ __launch_bounds__(kTailRows * kWave) void k_route_tail(int N, int nblk,
-                                                                  const int32_t *__restrict__ hist_part,
-                                                                  double *__restrict__ p_partial,
-                                                                  int32_t *__restrict__ counts) {
-    __shared__ int32_t hs[kTailRows][kWave];
-    __shared__ double ps[kTailRows][kWave];
-    const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
-    const int e = blockIdx.x * kWave + c;
+// block = 16 experts x 64 lanes of rows; lane r adds rows r, r + 64, ... in
+// order, then the 64 lane sums are added by a fixed binary tree (a fixed
+// order, so the score sums do not depend on timing).  Spreading the experts
+// over N'/16 blocks keeps hundreds of rows' loads in flight.  The score sums
+// go to row nblk of p_partial, where moe_balance_stats reads them.
+constexpr int kTailExperts = 16, kTailRows = 64;
+__global__ __launch_bounds__(kTailExperts * kTailRows) void k_route_tail(
+    int N, int nblk, const int32_t *__restrict__ hist_part, double *__restrict__ p_partial,
+    int32_t *__restrict__ counts) {
+    __shared__ int32_t hs[kTailRows][kTailExperts];
+    __shared__ double ps[kTailRows][kTailExperts];
+    const int c = threadIdx.x % kTailExperts, r = threadIdx.x / kTailExperts;
+    const int e = blockIdx.x * kTailExperts + c;
     int h = 0;
     double p = 0.0;
     if (e < N) {
@@ -405,15 +405,16 @@ __global__ __launch_bounds__(kTailRows * kWave) void k_route_tail(int N, int nbl
     hs[r][c] = h;
     ps[r][c] = p;
     __syncthreads();
-    if (r == 0 && e < N) {
-        int H = 0;
-        double S = 0.0;
-        for (int q = 0; q < kTailRows; ++q) {
-            H += hs[q][c];
-            S += ps[q][c];
+    for (int o = kTailRows / 2; o > 0; o >>= 1) {
+        if (r < o) {
+            hs[r][c] += hs[r + o][c];
+            ps[r][c] += ps[r + o][c];
         }
-        counts[e] = H;
-        if (p_partial) p_partial[(size_t)nblk * N + e] = S;
+        __syncthreads();
+    }
+    if (r == 0 && e < N) {
+        counts[e] = hs[0][c];
+        if (p_partial) p_partial[(size_t)nblk * N + e] = ps[0][c];
     }
 }
 
@@ -443,8 +444,9 @@ hipError_t launch_select(const moe_config &c, const float *logits, int splits, s
     else MOE_SEL(16);
 #undef MOE_SEL_SC
 #undef MOE_SEL
-    hipLaunchKernelGGL(k_route_tail, dim3((c.n_routed + kWave - 1) / kWave), dim3(kTailRows * kWave),
-                       0, s, c.n_routed, select_blocks(c), hist_part, p_partial, counts);
+    hipLaunchKernelGGL(k_route_tail, dim3((c.n_routed + kTailExperts - 1) / kTailExperts),
+                       dim3(kTailExperts * kTailRows), 0, s, c.n_routed, select_blocks(c), hist_part,
+                       p_partial, counts);
     return hipGetLastError();
 }
 

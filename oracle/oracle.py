@@ -33,6 +33,9 @@ import numpy as np
 HERE = Path(__file__).resolve().parent
 SRC = HERE / "oracle.c"
 LIB = HERE / "liboracle.so"
+# A prebuilt copy of this oracle to load instead (the sanitizer test builds
+# one with AddressSanitizer and UndefinedBehaviorSanitizer); not rebuilt here.
+LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
 
 SCORING = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "hash": 3}
 DTYPES = {"f32": 0, "bf16": 1}
@@ -57,9 +60,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
-        build()
-    lib = ctypes.CDLL(str(LIB))
+    if LIB_OVERRIDE:
+        lib = ctypes.CDLL(LIB_OVERRIDE)
+    else:
+        if not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
+            build()
+        lib = ctypes.CDLL(str(LIB))
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     lib.oracle_router_logits.argtypes = [i64, vp, i64, i64, i32, vp, vp, vp]
     lib.oracle_router_logits.restype = None

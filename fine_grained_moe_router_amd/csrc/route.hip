@@ -157,24 +157,73 @@ __device__ __forceinline__ double score_pointwise(int scoring, float l) {
     return sqrt(sp);
 }
 
-// Raw logits of one token held by one wavefront: lane `lane` owns experts
-// lane + 64 j, j < J.  The logit is row[e], or with a split router GEMM the
-// sum of its `splits` partials row[e] + row[stride + e] + ..., added in
-// split order in fp32 (so it is one fixed value whoever reads it).
+// A wavefront holds one token's N' experts: lane `lane` owns the J
+// consecutive experts J lane .. J lane + J - 1 (those below N'), so a row of
+// logits (or a split partial) arrives in one, two or four wide loads per
+// lane rather than J narrow ones.
+template <int J>
+__device__ __forceinline__ int lane_expert(int lane, int j) { return J * lane + j; }
+
+// J consecutive floats from p, in 16- or 8-byte loads where J allows (p
+// must then be aligned to them; see wave_token_logits).
+template <int J>
+__device__ __forceinline__ void load_row_part(const float *p, float (&v)[J]) {
+    if constexpr (J % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < J; j += 4) {
+            const float4 q = *(const float4 *)(p + j);
+            v[j] = q.x;
+            v[j + 1] = q.y;
+            v[j + 2] = q.z;
+            v[j + 3] = q.w;
+        }
+    } else if constexpr (J % 2 == 0) {
+#pragma unroll
+        for (int j = 0; j < J; j += 2) {
+            const float2 q = *(const float2 *)(p + j);
+            v[j] = q.x;
+            v[j + 1] = q.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) v[j] = p[j];
+    }
+}
+
+// Raw logits of one token held by one wavefront (lane_expert).  The logit is
+// row[e], or with a split router GEMM the sum of its `splits` partials
+// row[e] + row[stride + e] + ..., added in split order in fp32 (so it is one
+// fixed value whoever reads it).  A lane whose experts all exist loads them
+// whole; the lane holding the end of a ragged N' loads one by one.
 template <int J>
 __device__ __forceinline__ void wave_token_logits(int N, const float *row, int splits,
                                                   size_t stride, int lane, float (&raw)[J]) {
+    const int e0 = lane_expert<J>(lane, 0);
+    // whole-lane loads need every expert present and an aligned start: every
+    // row is 16-byte aligned when the buffer is and N' is a multiple of 4
+    const bool aligned = ((uintptr_t)row & 15) == 0 && ((stride & 3) == 0 || splits == 1);
+    const bool whole = e0 + J <= N && ((N % 4 == 0 && aligned) || J == 1);
+    if (whole) {
+        load_row_part<J>(row + e0, raw);
+        for (int z = 1; z < splits; ++z) {
+            float pz[J];
+            load_row_part<J>(row + (size_t)z * stride + e0, pz);
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int e = lane + 64 * j;
-        raw[j] = (e < N) ? row[e] : -INFINITY;
-    }
-    for (int z = 1; z < splits; ++z) {
-        const float *pz = row + (size_t)z * stride;
+            for (int j = 0; j < J; ++j) raw[j] += pz[j];
+        }
+    } else {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = lane + 64 * j;
-            if (e < N) raw[j] += pz[e];
+            const int e = e0 + j;
+            raw[j] = (e < N) ? row[e] : -INFINITY;
+        }
+        for (int z = 1; z < splits; ++z) {
+            const float *pz = row + (size_t)z * stride;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int e = e0 + j;
+                if (e < N) raw[j] += pz[e];
+            }
         }
     }
 }
@@ -188,7 +237,7 @@ __device__ __forceinline__ void wave_token_scores(int N, int scoring, const floa
                                                   float (&s32)[J]) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int e = lane + 64 * j;
+        const int e = lane_expert<J>(lane, j);
         float v = raw[j];
         if (offset && e < N) v = v + offset[e];  // fp32 add
         l[j] = v;
@@ -201,7 +250,7 @@ __device__ __forceinline__ void wave_token_scores(int N, int scoring, const floa
         double ex[J], part = 0.0;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = lane + 64 * j;
+            const int e = lane_expert<J>(lane, j);
             ex[j] = (e < N) ? exp((double)l[j] - (double)m) : 0.0;
             part += ex[j];
         }
@@ -211,7 +260,7 @@ __device__ __forceinline__ void wave_token_scores(int N, int scoring, const floa
     } else {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = lane + 64 * j;
+            const int e = lane_expert<J>(lane, j);
             s32[j] = (e < N) ? (float)score_pointwise(scoring, l[j]) : 0.0f;
         }
     }
@@ -244,7 +293,11 @@ __device__ __forceinline__ void wave_argmax(float &v, int &idx) {
     idx = __builtin_amdgcn_readlane(idx, 63);
 }
 
-// One wavefront per token.  Lane `lane` owns experts lane + 64 j, j < J.
+// One wavefront per token.  Lane `lane` owns experts lane_expert(lane, j),
+// j < J (J consecutive experts: a split partial's row arrives in one wide
+// load per lane; V3 prefill select 47 -> 41 us, decode 30 -> 20 us).  Two
+// tokens per wave side by side was measured and is slower: the extra
+// registers cost more occupancy than the overlapped argmax chains gain.
 // Node-limited routing (n_groups > 0): the experts of the topk_groups groups
 // with the largest best key are the only candidates; the others are marked
 // taken before the top-K' rounds.
@@ -277,12 +330,12 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
         if (lg_out) {
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                if (lane + 64 * j < N) lg_out[(size_t)t * N + lane + 64 * j] = raw[j];
+                if (lane_expert<J>(lane, j) < N) lg_out[(size_t)t * N + lane_expert<J>(lane, j)] = raw[j];
         }
         wave_token_scores<J>(N, SC, raw, offset, lane, l, s32);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = lane + 64 * j;
+            const int e = lane_expert<J>(lane, j);
             key[j] = bias ? ((e < N) ? s32[j] + bias[e] : -INFINITY) : l[j];  // fp32 add
             if (e < N) pacc[j] += (double)s32[j];
         }
@@ -291,7 +344,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
             // best key of each group (lane g holds group g), via this wave's LDS row
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                if (lane + 64 * j < N) kbuf[wave][lane + 64 * j] = key[j];
+                if (lane_expert<J>(lane, j) < N) kbuf[wave][lane_expert<J>(lane, j)] = key[j];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -313,7 +366,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
             }
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const int e = lane + 64 * j;
+                const int e = lane_expert<J>(lane, j);
                 if (e < N && !((chosen >> (e / gsz)) & 1ull)) taken |= 1u << j;
             }
         }
@@ -329,7 +382,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
                 int bi = 0x7fffffff;
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    const int e = lane + 64 * j;
+                    const int e = lane_expert<J>(lane, j);
                     if (e < N && !((taken >> j) & 1u) && (key[j] > bk || bi == 0x7fffffff)) {
                         bk = key[j];
                         bi = e;
@@ -339,12 +392,12 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
                 float mine = 0.0f;
 #pragma unroll
                 for (int j = 0; j < J; ++j)
-                    if (lane + 64 * j == bi) {
+                    if (lane_expert<J>(lane, j) == bi) {
                         taken |= 1u << j;
                         mine = s32[j];
                     }
                 sel[k] = bi;
-                sv[k] = __shfl(mine, bi & 63, kWave);
+                sv[k] = __shfl(mine, bi / J, kWave);   // the lane that owns expert bi
             }
         }
         // ---- gates: s, or s / (double sum of the selected s in k order)
@@ -366,7 +419,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
     // in a fixed order), one row each for k_route_tail
     if (p_partial) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) psum[wave][lane + 64 * j] = pacc[j];
+        for (int j = 0; j < J; ++j) psum[wave][lane_expert<J>(lane, j)] = pacc[j];
     }
     __syncthreads();
     for (int e = threadIdx.x; e < N; e += blockDim.x) {
@@ -479,7 +532,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_scores(int T, int N, int 
     wave_token_scores<J>(N, scoring, raw, offset, lane, l, s32);
 #pragma unroll
     for (int j = 0; j < J; ++j)
-        if (lane + 64 * j < N) s32_out[(size_t)t * N + lane + 64 * j] = s32[j];
+        if (lane_expert<J>(lane, j) < N) s32_out[(size_t)t * N + lane_expert<J>(lane, j)] = s32[j];
 }
 
 __device__ __forceinline__ void seg_range(const int32_t *off, int s, int T, int &t0, int &t1) {

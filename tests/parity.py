@@ -15,6 +15,7 @@ from oracle import oracle as O
 # 1e-4 excluded.  fp32: max-abs 1e-4, rel-L2 1e-5, gap threshold 1e-6.
 TOL = {"bf16": dict(max_abs=2e-2, rel_l2=5e-3, gap=1e-4),
        "f32": dict(max_abs=1e-4, rel_l2=1e-5, gap=1e-6)}
+ROW_TILE = 256          # rows per row tile of the bf16 expert GEMMs
 
 
 def gpu_layer(cfg: LayerConfig, inp: LayerInputs, logits_out: bool = True):
@@ -91,3 +92,32 @@ def compare_h(cfg: LayerConfig, h_gpu: np.ndarray, h_ref: np.ndarray, gap: np.nd
 
 def gpu_h_as_f64(h: torch.Tensor) -> np.ndarray:
     return h.detach().float().cpu().numpy().astype(np.float64)
+
+
+def row_tile_tokens(idx: np.ndarray, T: int, n_routed: int, has_shared: bool) -> np.ndarray:
+    """Tokens at the first and the last row of every row tile of every group:
+    a routed expert's rows are its (token, slot) pairs in pair order, dealt
+    over R = ceil(rows / 256) row tiles in whole 32-row fragments (32
+    ceil(rows / (32 R)) rows per tile, the rest in the last); the shared
+    group's rows are the tokens in order, 256 per tile."""
+    K = idx.shape[1]
+    pairs = np.argsort(idx.ravel(), kind="stable")
+    ids = idx.ravel()[pairs]
+    out = set()
+    for e in range(n_routed):
+        lo, hi = np.searchsorted(ids, [e, e + 1])
+        cnt = hi - lo
+        if cnt == 0:
+            continue
+        R = -(-cnt // ROW_TILE)
+        rpt = min(ROW_TILE, 32 * (-(-cnt // (32 * R))))
+        for i in range(R):
+            a, b = i * rpt, min(cnt, (i + 1) * rpt) - 1
+            if a > b:
+                continue
+            out.add(int(pairs[lo + a]) // K)
+            out.add(int(pairs[lo + b]) // K)
+    if has_shared:
+        for t0 in range(0, T, ROW_TILE):
+            out.update((t0, min(T, t0 + ROW_TILE) - 1))
+    return np.array(sorted(out), np.int64)

@@ -17,7 +17,8 @@ from fine_grained_moe_router_amd.configs import CONFIGS, scaled
 from fine_grained_moe_router_amd.synth import make_inputs, to_numpy
 from oracle import oracle as O
 
-from parity import (compare_h, gpu_h_as_f64, gpu_layer, host, oracle_h, oracle_route_tokens)
+from parity import (ROW_TILE, compare_h, gpu_h_as_f64, gpu_layer, host, oracle_h,
+                    oracle_route_tokens, row_tile_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -255,7 +256,6 @@ def test_segmentation_identity_on_gpu():
 # each 256-token slice of the shared group.
 
 FULL = ["v3_decode", "mid", "v3_prefill", "v4_skew", "v4_hash"]
-ROW_TILE = 256          # rows per row tile of the bf16 expert GEMMs
 _STATE = {}             # the one full-size workload kept between tests
 
 
@@ -276,35 +276,6 @@ def full_state(cfg):
           "idx": to_numpy(r["idx"])}
     _STATE[cfg.name] = st
     return st
-
-
-def row_tile_tokens(idx: np.ndarray, T: int, n_routed: int, has_shared: bool) -> np.ndarray:
-    """Tokens at the first and the last row of every row tile of every group:
-    a routed expert's rows are its (token, slot) pairs in pair order, dealt
-    over R = ceil(rows / 256) row tiles in whole 32-row fragments (32
-    ceil(rows / (32 R)) rows per tile, the rest in the last); the shared
-    group's rows are the tokens in order, 256 per tile."""
-    K = idx.shape[1]
-    pairs = np.argsort(idx.ravel(), kind="stable")
-    ids = idx.ravel()[pairs]
-    out = set()
-    for e in range(n_routed):
-        lo, hi = np.searchsorted(ids, [e, e + 1])
-        cnt = hi - lo
-        if cnt == 0:
-            continue
-        R = -(-cnt // ROW_TILE)
-        rpt = min(ROW_TILE, 32 * (-(-cnt // (32 * R))))
-        for i in range(R):
-            a, b = i * rpt, min(cnt, (i + 1) * rpt) - 1
-            if a > b:
-                continue
-            out.add(int(pairs[lo + a]) // K)
-            out.add(int(pairs[lo + b]) // K)
-    if has_shared:
-        for t0 in range(0, T, ROW_TILE):
-            out.update((t0, min(T, t0 + ROW_TILE) - 1))
-    return np.array(sorted(out), np.int64)
 
 
 def check_tokens(cfg, st, tokens):

@@ -24,6 +24,11 @@ workload.  Other modes:
                         expert-GEMM FLOP counts through the vendor library
                         (torch.matmul / torch.bmm), the attainable-rate
                         reference of the GPU the layer runs on.
+    --ep-share G        one JSON line timing one GPU's share of the layer
+                        under expert parallelism over G GPUs: the router on
+                        its own T tokens, its N'/G resident experts on the
+                        pairs that G T tokens send it, the shared expert on
+                        its own tokens (the exchange itself is not run).
 """
 from __future__ import annotations
 
@@ -117,6 +122,8 @@ def parse_args(argv=None):
     ap.add_argument("--extras", action="store_true",
                     help="time the entry points beyond the layer step (node-limited routing, "
                          "in-sequence and device-level statistics, bias update) instead")
+    ap.add_argument("--ep-share", type=int, default=0, metavar="G",
+                    help="time one GPU's share of the layer under expert parallelism over G GPUs")
     ap.add_argument("--calibrate", action="store_true",
                     help="time dense and batched bf16 GEMMs of the layer's expert-GEMM FLOP "
                          "counts through torch.matmul / torch.bmm (hipBLASLt), as the "
@@ -407,6 +414,134 @@ def extras(cfg):
     return 0
 
 
+def ep_share(cfg, gpus: int, steps: int, warmup: int):
+    """One JSON line: one GPU's share of the layer under expert parallelism
+    over `gpus` GPUs, at its real shape, with the kernels of the layer step.
+
+    Routed experts are split evenly and contiguously over the GPUs (GPU g
+    holds experts [g N'/G, (g+1) N'/G)); the router and the shared experts
+    are replicated; each GPU routes its own T tokens.  G T tokens (the
+    workload's seeded inputs, T per GPU) are routed once, untimed, to find
+    what each GPU receives: one row per (token, GPU) pair with at least one
+    of the GPU's experts among its K', that row's other slots out of range.
+    The GPU that receives the most pairs, the one that sets an expert-
+    parallel step's time, is measured.  Its step: moe_route over its own T
+    tokens; moe_forward on the received rows with its N'/G experts and no
+    shared expert; moe_forward of the shared expert over its own T tokens
+    (one group, gate 1: the same work as the shared group inside the
+    layer); moe_balance_stats.  The two all-to-all exchanges, and the final
+    add of the returned rows, are not run (one GPU).  The routed forward
+    also adds the received x row as a residual, which the returned
+    contribution would not carry: one row read and one add per row."""
+    import torch
+    from fine_grained_moe_router_amd import binding as B
+    from fine_grained_moe_router_amd.synth import make_inputs
+
+    T, N, K, d = cfg.T, cfg.n_routed, cfg.top_k, cfg.d_model
+    assert cfg.n_shared == 1 and cfg.scoring != "hash" and N % gpus == 0
+    n_loc = N // gpus
+    print(f"[ep-share] {cfg.name}: generating inputs for {gpus} x {T} tokens",
+          file=sys.stderr, flush=True)
+    all_cfg = cfg.with_(T=gpus * T)
+    inp = make_inputs(all_cfg, "cuda")
+    r = B.route(all_cfg, x=inp.x, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias,
+                want_pstat=False)
+    owner = r["idx"].long() // n_loc                          # [G T][K] destination GPU
+    pairs = torch.stack([(owner == g).sum() for g in range(gpus)]).cpu()
+    g = int(pairs.argmax())
+    local = owner == g
+    rows = local.any(dim=1).nonzero().squeeze(1)
+    R = int(rows.numel())
+    x_recv = inp.x[rows].contiguous()
+    idx_recv = torch.where(local[rows], r["idx"][rows] - g * n_loc,
+                           torch.full_like(r["idx"][rows], -1)).contiguous()
+    w_recv = r["w"][rows].contiguous()
+    counts = torch.bincount(idx_recv[idx_recv >= 0].long(), minlength=n_loc)
+    w13 = inp.w13[g * n_loc:(g + 1) * n_loc].contiguous()
+    w2 = inp.w2[g * n_loc:(g + 1) * n_loc].contiguous()
+    x_own = inp.x[g * T:(g + 1) * T].contiguous()
+    inp.w13 = inp.w2 = None
+    torch.cuda.empty_cache()
+
+    routed_cfg = cfg.with_(name=f"{cfg.name}_ep{gpus}_routed", T=R, n_routed=n_loc, n_shared=0)
+    shared_cfg = cfg.with_(name=f"{cfg.name}_ep{gpus}_shared", n_routed=1, top_k=1, n_shared=0,
+                           d_ff=cfg.d_ff_shared, bias=False, zipf_s=0.0)
+    idx_sh = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+    w_sh = torch.ones((T, 1), dtype=torch.float32, device="cuda")
+    ws_route = B.alloc_workspace(B.make_config(cfg), B.WS_ROUTE, "cuda")
+    ws_rt = B.alloc_workspace(B.make_config(routed_cfg), B.WS_FORWARD, "cuda")
+    ws_sh = B.alloc_workspace(B.make_config(shared_cfg), B.WS_FORWARD, "cuda")
+    route_out = {"idx": torch.empty((T, K), dtype=torch.int32, device="cuda"),
+                 "w": torch.empty((T, K), dtype=torch.float32, device="cuda"),
+                 "counts": torch.empty(N, dtype=torch.int32, device="cuda"),
+                 "pstat": torch.empty(B.workspace_bytes(B.make_config(cfg), B.WS_PSTAT),
+                                      dtype=torch.uint8, device="cuda")}
+    h_recv = torch.empty_like(x_recv)
+    h_own = torch.empty_like(x_own)
+    stats_out = {"f": torch.empty(N, dtype=torch.float32, device="cuda"),
+                 "P": torch.empty(N, dtype=torch.float32, device="cuda"),
+                 "loss": torch.empty(2, dtype=torch.float32, device="cuda")}
+
+    def route():
+        return B.route(cfg, x=x_own, w_gate=inp.w_gate, offset=inp.offset, bias=inp.bias,
+                       out=route_out, workspace=ws_route)
+
+    def routed():
+        B.forward(routed_cfg, x_recv, idx_recv, w_recv, w13, w2, h=h_recv, workspace=ws_rt)
+
+    def shared():
+        B.forward(shared_cfg, x_own, idx_sh, w_sh, inp.w13s, inp.w2s, h=h_own, workspace=ws_sh)
+
+    def step():
+        rr = route()
+        routed()
+        shared()
+        B.balance_stats(cfg, rr["counts"], rr["pstat"], out=stats_out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[ep-share] GPU {g}: {R} rows, {int(pairs[g])} pairs; timing {steps} steps",
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+
+    # per-call stage times: each call alone, the library's HIP events
+    parts = {}
+    for name, fn in (("route", route), ("routed_forward", routed), ("shared_forward", shared)):
+        B.profile_enable(16 * steps)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        st = B.profile_collect()
+        parts[name] = {k: v["ms"] / v["launches"] for k, v in st.items() if v["launches"]}
+
+    P = int(pairs[g])
+    f = cfg.d_ff
+    gemm = {}
+    for stage, flop, wbytes in (("gate_up", 4 * d * f * P, n_loc * 2 * f * d * 2),
+                                ("down", 2 * d * f * P, n_loc * d * f * 2)):
+        t = parts["routed_forward"][stage] * 1e-3
+        gemm[stage] = {"kernel": KERNEL_OF_STAGE[stage], "ms": t * 1e3,
+                       "tflops": flop / t / 1e12, "mfma_frac": flop / t / 1e12 / PEAK_BF16_TFLOPS,
+                       "weight_gbs": wbytes / t / 1e9}
+    print(json.dumps({
+        "mode": "ep_share", "workload": cfg.name, "gpus": gpus, "gpu": g,
+        "tokens_per_gpu": T, "experts_per_gpu": n_loc,
+        "pairs_per_gpu": [int(v) for v in pairs], "rows_received": R, "pairs_received": P,
+        "rows_per_expert_mean": P / n_loc,
+        "max_over_mean_load": float(counts.max()) / max(float(counts.float().mean()), 1e-9),
+        "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "tokens_per_s_per_gpu_exchange_excluded": T / (ms * 1e-3),
+        "calls_ms": parts, "routed_gemms": gemm,
+        "note": "the two all-to-all exchanges are not run; the routed forward adds a residual "
+                "the returned rows would not carry"}))
+    return 0
+
+
 def calibrate(reps: int):
     """One JSON line: TFLOP/s of bf16 GEMMs through the vendor library
     (torch.matmul / torch.bmm -> hipBLASLt) on random normal operands, with
@@ -465,6 +600,8 @@ def main(argv=None):
         return extras(cfg)
     if args.calibrate:
         return calibrate(args.steps)
+    if args.ep_share:
+        return ep_share(cfg, args.ep_share, args.steps, args.warmup)
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     layer = Layer(cfg)
     torch.cuda.synchronize()

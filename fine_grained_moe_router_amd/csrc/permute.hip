@@ -265,26 +265,53 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int N, int T, int n_shared, 
     }
 }
 
-// Stable placement: thread e scans its chunk's ids in pair order and writes
-// every pair that chose e (and its gate) to the next row of expert e.
-__global__ __launch_bounds__(256) void k_perm_scatter(int P, int N, int chunk,
-                                                      const int32_t *__restrict__ idx,
-                                                      const float *__restrict__ topk_w,
-                                                      const int32_t *__restrict__ cc,
-                                                      const int32_t *__restrict__ group_off,
-                                                      int32_t *__restrict__ perm,
-                                                      float *__restrict__ gsort) {
-    extern __shared__ int32_t ids[];
-    const int p0 = blockIdx.x * chunk, n = min(P, p0 + chunk) - p0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) ids[i] = idx[p0 + i];
+// Stable placement, one wavefront per chunk.  The chunk's pairs are taken
+// 64 at a time in pair order, one per lane.  A lane whose pair chose expert
+// e writes it (and its gate) to row
+//     group_off[e] + (pairs of e in earlier chunks) + (pairs of e before it
+//     in this chunk),
+// the last term being a running count per expert in LDS plus the number of
+// lower lanes in the same 64 that chose e.  The lanes that chose e are found
+// by matching e bit by bit, one ballot per bit of N' - 1; the highest of them
+// then advances e's count.  Out-of-range ids are skipped.
+__global__ __launch_bounds__(64) void k_perm_scatter(int P, int N, int chunk,
+                                                     const int32_t *__restrict__ idx,
+                                                     const float *__restrict__ topk_w,
+                                                     const int32_t *__restrict__ cc,
+                                                     const int32_t *__restrict__ group_off,
+                                                     int32_t *__restrict__ perm,
+                                                     float *__restrict__ gsort) {
+    extern __shared__ int32_t next_row[];   // [N']
+    const int lane = threadIdx.x;
+    for (int e = lane; e < N; e += 64)
+        next_row[e] = group_off[e] + cc[(size_t)blockIdx.x * N + e];
     __syncthreads();
-    for (int e = threadIdx.x; e < N; e += blockDim.x) {
-        int pos = group_off[e] + cc[(size_t)blockIdx.x * N + e];
-        for (int i = 0; i < n; ++i)
-            if (ids[i] == e) {
-                perm[pos] = p0 + i;
-                gsort[pos++] = topk_w[p0 + i];
-            }
+    const int bits = N > 1 ? 32 - __clz(N - 1) : 0;
+    const uint64_t below = (1ull << lane) - 1;
+    const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+    int p = p0 + lane;
+    int e = p < p1 ? idx[p] : -1;
+    float g = p < p1 ? topk_w[p] : 0.f;
+    for (int base = p0; base < p1; base += 64, p += 64) {
+        // the next 64 pairs' loads are in flight while these are placed
+        const int pn = p + 64;
+        const int en = pn < p1 ? idx[pn] : -1;
+        const float gn = pn < p1 ? topk_w[pn] : 0.f;
+        const bool ok = e >= 0 && e < N;
+        uint64_t same = __ballot(ok);
+        for (int b = 0; b < bits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(ok && bit);
+            same &= bit ? m : ~m;
+        }
+        if (ok) {
+            const int row = next_row[e] + __popcll(same & below);
+            perm[row] = p;
+            gsort[row] = g;
+            if ((same >> lane) == 1ull) next_row[e] = row + 1;   // highest lane of e's set
+        }
+        e = en;
+        g = gn;
     }
 }
 
@@ -304,7 +331,7 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, c.T, c.n_shared, c.d_ff,
                        c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
                        z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (RowTileDesc *)(ws + L.off_rtd));
-    hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(256), (size_t)L.chunk * 4, s, P, N,
+    hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(64), (size_t)N * 4, s, P, N,
                        L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
                        (float *)(ws + L.off_gsort));
     return hipGetLastError();

@@ -151,3 +151,20 @@ def to_numpy(t: Optional[torch.Tensor]):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def make_share_routing(rows: int, n_local: int, top_k: int, seed: int = 0):
+    """A seeded caller routing of the shape one GPU receives under expert
+    parallelism (host tensors): row r names c_r distinct experts of the
+    n_local resident ones, c_r uniform in 1..top_k, in random slots; the
+    other slots hold -1 (no expert); gates uniform in [0, 1)."""
+    g = _gen("cpu", seed, "share_routing", rows, n_local, top_k)
+    n = torch.randint(1, top_k + 1, (rows,), generator=g)
+    experts = torch.argsort(torch.rand((rows, n_local), generator=g), dim=1)[:, :top_k]
+    slots = torch.argsort(torch.rand((rows, top_k), generator=g), dim=1)
+    keep = torch.arange(top_k).unsqueeze(0) < n.unsqueeze(1)
+    idx = torch.full((rows, top_k), -1, dtype=torch.int32)
+    idx.scatter_(1, slots, torch.where(keep, experts, -1).to(torch.int32))
+    gate = torch.rand((rows, top_k), generator=g).float()
+    return idx, gate
+

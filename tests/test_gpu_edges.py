@@ -9,6 +9,9 @@
   d = 256), the permutation's largest chunks and ~16k row tiles per GEMM.
 * Node-limited routing at the full V4 shape on the V4 book's layout (384
   experts on 32 nodes of 12, at most M = 4 nodes per token).
+* One GPU's share of the V3 layer under 8-way expert parallelism: 32
+  resident experts at full width on received rows that name 1 to 8 of them
+  (the other slots empty), about 2,300 rows per expert.
 Routing is checked bit-exactly on identical logits for every token; the
 layer output on the first and last row of every row tile of every group
 (a seeded subset of them for the largest batch)."""
@@ -18,7 +21,7 @@ import torch
 
 from fine_grained_moe_router_amd import binding as B
 from fine_grained_moe_router_amd.configs import CONFIGS, scaled
-from fine_grained_moe_router_amd.synth import make_inputs, to_numpy
+from fine_grained_moe_router_amd.synth import make_inputs, make_share_routing, to_numpy
 from oracle import oracle as O
 
 from parity import (compare_h, gpu_h_as_f64, gpu_layer, host, oracle_h, oracle_route_tokens,
@@ -40,6 +43,7 @@ def check_routing(cfg, inp, r):
 
 
 def check_layer(cfg, inp, r, tokens):
+    """h on the listed tokens against the oracle's routing and layer."""
     x_h = host(inp.x)
     _, idx, gate, _, gap = oracle_route_tokens(cfg, inp, tokens, x_h=x_h)
     h_ref = oracle_h(cfg, inp, tokens, idx, gate, x_h=x_h)
@@ -92,3 +96,24 @@ def test_v4_book_node_layout_full_size():
     replaced = np.mean([len(set(a) - set(b)) for a, b in zip(p, idx)]) / cfg.top_k
     print(f"[edges] v4 node limit: replaced share {replaced:.3f}", flush=True)
     assert replaced > 0.05
+
+
+def test_ep_share_shape():
+    """The routed part of one GPU's share under 8-way expert parallelism at
+    the V3 width: 16,384 received rows over 32 resident experts, each row
+    naming 1..8 of them in random slots (the rest -1), no shared expert;
+    the first and last row of every row tile against the oracle."""
+    cfg = CONFIGS["v3_prefill"].with_(name="v3_ep8_routed", T=16384, n_routed=32, n_shared=0)
+    print(f"[edges] {cfg.name}", flush=True)
+    inp = make_inputs(cfg, "cuda")
+    idx, gate = make_share_routing(cfg.T, cfg.n_routed, cfg.top_k, seed=3)
+    h = B.forward(cfg, inp.x, idx.cuda(), gate.cuda(), inp.w13, inp.w2)
+    torch.cuda.synchronize()
+    idx_np, gate_np = idx.numpy(), gate.numpy()
+    tokens = row_tile_tokens(idx_np, cfg.T, cfg.n_routed, False)
+    valid = idx_np[tokens] >= 0
+    h_ref = oracle_h(cfg, inp, tokens, np.where(valid, idx_np[tokens], 0),
+                     np.where(valid, gate_np[tokens], 0))
+    res = compare_h(cfg, gpu_h_as_f64(h)[tokens], h_ref, np.full(len(tokens), np.inf))
+    print(f"[edges] {cfg.name}: tokens {len(tokens)} max_abs {res[0]:.4g} rel_l2 {res[1]:.4g}",
+          flush=True)

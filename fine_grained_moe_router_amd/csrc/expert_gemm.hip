@@ -39,7 +39,19 @@ __device__ __forceinline__ int find_group(const int32_t *__restrict__ base, int 
 struct TileJob {
     int g, i, j, row0, nrows, goff;
     bool shared;
+    bool single;    // the group's only row tile
 };
+
+// Whether a tile's weight loads are non-temporal: when its group has a
+// single row tile, no other tile reads its weight tile, and marking those
+// loads non-temporal leaves L2 to the token rows, which the group's other
+// column tiles read again.  Applied to thin tiles (at most 64 rows, where
+// the weight stream dominates; the kernels instantiate the policy for the
+// one- and zero-fragment waves only).
+constexpr int kStreamRows = 64;
+__device__ __forceinline__ bool streams_weights(const TileJob &tj) {
+    return tj.single && tj.nrows <= kStreamRows;
+}
 
 __device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, int bm) {
     TileJob t;
@@ -53,6 +65,7 @@ __device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, i
     t.row0 = t.i * bm;
     t.nrows = min(bm, cnt - t.row0);
     t.shared = (t.g == a.n_routed);
+    t.single = (mt == 1);
     t.goff = t.shared ? 0 : a.group_off[t.g];
     return t;
 }
@@ -274,13 +287,14 @@ __device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
     return o;
 }
 
-// One gate/up tile whose wave computes NF row fragments.
-template <class P, int NF>
+// One gate/up tile whose wave computes NF row fragments (STREAM_B: its
+// weight tile is read by no other tile).
+template <class P, int NF, bool STREAM_B>
 __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                             const OperandRows<P> &rows, int zc0, int zw,
                                             size_t rbase, int k) {
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
-    pipe_gemm_nf<P, true, NF>(lds, rows, a.d, 0, 1, 0, 0, acc);
+    pipe_gemm_nf<P, true, NF, false, STREAM_B>(lds, rows, a.d, 0, 1, 0, 0, acc);
     const int ticket = threadIdx.x == 0 ? take_ticket(a, k) : 0;
     // SwiGLU epilogue: z = SiLU(W1 u) * (W3 u) in fp32 (the sigmoid from the
     // hardware exponential and reciprocal, each within about an ulp), rounded
@@ -349,6 +363,7 @@ __device__ __forceinline__ TileJob row_tile(const GroupedArgs &a, const RowTileD
     t.nrows = min(rpt, cnt - t.row0);
     t.goff = d.goff;
     t.shared = (t.g == a.n_routed);
+    t.single = (R == 1);
     return t;
 }
 
@@ -386,12 +401,17 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
         rows.boff[l] = ((uint32_t)js * 2 * wwidth + (up ? wwidth : 0) + c) * (uint32_t)a.d;
     }
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
+    const bool stream_b = streams_weights(tj);
     switch (wave_frags<P>(tj.nrows)) {
-        case 4: return gate_up_tile<P, 4>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 3: return gate_up_tile<P, 3>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 2: return gate_up_tile<P, 2>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 1: return gate_up_tile<P, 1>(a, tj, lds, rows, zc0, zw, rbase, k);
-        default: return gate_up_tile<P, 0>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 4: return gate_up_tile<P, 4, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 3: return gate_up_tile<P, 3, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 2: return gate_up_tile<P, 2, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 1:
+            return stream_b ? gate_up_tile<P, 1, true>(a, tj, lds, rows, zc0, zw, rbase, k)
+                            : gate_up_tile<P, 1, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        default:
+            return stream_b ? gate_up_tile<P, 0, true>(a, tj, lds, rows, zc0, zw, rbase, k)
+                            : gate_up_tile<P, 0, false>(a, tj, lds, rows, zc0, zw, rbase, k);
     }
 }
 
@@ -424,16 +444,16 @@ __device__ __forceinline__ int stage_offset(int row, int col) {
 // the tile staged in LDS (the A stages and the first two B stages), then
 // each wave stores two whole rows of 512 bytes at a time with 16-byte lane
 // stores.  A value beyond fp16's range (rare) is also stored as fp32.
-template <class P, int NF>
+template <class P, int NF, bool STREAM_B>
 __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                          const OperandRows<P> &rows, int K, int split, int n0,
                                          int my_pair, float my_gate, int k) {
     f32x16 acc[NF > 0 ? NF : 1][P::FN];
     if (tj.shared)
-        pipe_gemm_nf<P, false, NF, true>(lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs,
-                                         split ? K / 2 : 0, acc);
+        pipe_gemm_nf<P, false, NF, true, STREAM_B>(lds, rows, K, a.fs, a.n_shared,
+                                                   (size_t)a.d * a.fs, split ? K / 2 : 0, acc);
     else
-        pipe_gemm_nf<P, false, NF, true>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
+        pipe_gemm_nf<P, false, NF, true, STREAM_B>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
     int32_t *rdst = (int32_t *)(lds + tile_info_offset<P>());   // destination row
     float *rgate = (float *)(lds + tile_info_offset<P>() + 4 * P::BM);
     if (threadIdx.x < P::BM) {
@@ -567,12 +587,21 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
         my_pair = a.perm[rbase + threadIdx.x];
         my_gate = a.gsort[rbase + threadIdx.x];
     }
+    // a split tile reads each W2 tile twice in a row (once per half), the
+    // second time from L2: it keeps the default policy
+    const bool stream_b = streams_weights(tj) && !split;
     switch (wave_frags<P>(tj.nrows)) {
-        case 4: return down_tile<P, 4>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 3: return down_tile<P, 3>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 2: return down_tile<P, 2>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 1: return down_tile<P, 1>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        default: return down_tile<P, 0>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 4: return down_tile<P, 4, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 3: return down_tile<P, 3, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 2: return down_tile<P, 2, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 1:
+            return stream_b
+                       ? down_tile<P, 1, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k)
+                       : down_tile<P, 1, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        default:
+            return stream_b
+                       ? down_tile<P, 0, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k)
+                       : down_tile<P, 0, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
     }
 }
 

@@ -134,9 +134,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Cache policy of an operand load: the default, or non-temporal (the `nt`
+// bit) for data no other load will read again, so that its lines are the
+// first to leave L2.
+constexpr int kCpolDefault = 0, kCpolStream = 2;
+
+template <int CPOL = kCpolDefault>
 __device__ __forceinline__ void load_lds16(const uint16_t *src, char *lds_dst) {
     __builtin_amdgcn_global_load_lds((const void *)src,
-                                     (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+                                     (__attribute__((address_space(3))) void *)lds_dst, 16, 0, CPOL);
 }
 // The same from a wave-uniform base plus a 32-bit byte offset: the form the
 // instruction takes natively (64-bit base in scalar registers, one vector
@@ -148,9 +154,10 @@ __device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return (const uint16_t *)(((uint64_t)hi << 32) | lo);
 }
+template <int CPOL = kCpolDefault>
 __device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byte_off,
                                               char *lds_dst) {
-    load_lds16((const uint16_t *)((const char *)base + byte_off), lds_dst);
+    load_lds16<CPOL>((const uint16_t *)((const char *)base + byte_off), lds_dst);
 }
 
 // Run the K loop of one tile.  A rows past the valid count are not fetched
@@ -161,8 +168,9 @@ __device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byt
 // fewer MFMAs.  B's k offset of k-tile k0 is k0, or
 // ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several matrices
 // side by side along K, possibly repeated).  AFF: both operands are affine
-// (rows.aoff[0], rows.astep; rows.boff[0], rows.bstep).
-template <class P, bool SPLIT, int NF, bool AFF = false>
+// (rows.aoff[0], rows.astep; rows.boff[0], rows.bstep).  STREAM_B: B is
+// read by this tile alone and once, so its loads are non-temporal.
+template <class P, bool SPLIT, int NF, bool AFF = false, bool STREAM_B = false>
 __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &rows, int K,
                                              int bsplit, int bmod, size_t bstride, int a_half,
                                              f32x16 (&acc)[NF > 0 ? NF : 1][P::FN]) {
@@ -233,8 +241,8 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
                           a_lds + stage_off + (n * P::NT + wave * 64) * 16);
     };
     auto b_load = [&](int n, uint32_t kbyte, uint32_t stage_off) {
-        load_lds16_at(bbase, b_byte(n) + kbyte,
-                      b_lds + stage_off + (n * P::NT + wave * 64) * 16);
+        load_lds16_at<STREAM_B ? kCpolStream : kCpolDefault>(
+            bbase, b_byte(n) + kbyte, b_lds + stage_off + (n * P::NT + wave * 64) * 16);
     };
     const int nk = K / P::BK;
 #pragma unroll

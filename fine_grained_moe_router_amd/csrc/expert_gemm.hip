@@ -44,16 +44,10 @@ struct TileJob {
 
 // Whether a tile's weight loads are non-temporal: when its group has a
 // single row tile, no other tile reads its weight tile, so its weight lines
-// need not be kept for reuse.  Applied to thin tiles (at most 64 rows, where
-// the weight stream dominates; the kernels instantiate the policy for the
-// one- and zero-fragment waves only).  The bytes fetched past L2 stay the
-// same; what changes is beyond L2 (the Infinity Cache's allocation, which
-// the L2 counters do not separate from HBM), and thin-tile launches run
-// 7-10% faster.
-constexpr int kStreamRows = 64;
-__device__ __forceinline__ bool streams_weights(const TileJob &tj) {
-    return tj.single && tj.nrows <= kStreamRows;
-}
+// need not be kept for reuse.  The bytes fetched past L2 stay the same; what
+// changes is beyond L2 (the Infinity Cache's allocation, which the L2
+// counters do not separate from HBM): thin-tile launches run 7-10% faster.
+__device__ __forceinline__ bool streams_weights(const TileJob &tj) { return tj.single; }
 
 __device__ __forceinline__ TileJob decode_tile(const GroupedArgs &a, int tile, int bm) {
     TileJob t;
@@ -404,16 +398,17 @@ __device__ __forceinline__ int gate_up_body(const GroupedArgs &a, const TileJob 
     }
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
     const bool stream_b = streams_weights(tj);
-    switch (wave_frags<P>(tj.nrows)) {
+    switch (wave_frags<P>(tj.nrows) + (stream_b ? 5 : 0)) {
         case 4: return gate_up_tile<P, 4, false>(a, tj, lds, rows, zc0, zw, rbase, k);
         case 3: return gate_up_tile<P, 3, false>(a, tj, lds, rows, zc0, zw, rbase, k);
         case 2: return gate_up_tile<P, 2, false>(a, tj, lds, rows, zc0, zw, rbase, k);
-        case 1:
-            return stream_b ? gate_up_tile<P, 1, true>(a, tj, lds, rows, zc0, zw, rbase, k)
-                            : gate_up_tile<P, 1, false>(a, tj, lds, rows, zc0, zw, rbase, k);
-        default:
-            return stream_b ? gate_up_tile<P, 0, true>(a, tj, lds, rows, zc0, zw, rbase, k)
-                            : gate_up_tile<P, 0, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 1: return gate_up_tile<P, 1, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 0: return gate_up_tile<P, 0, false>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 9: return gate_up_tile<P, 4, true>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 8: return gate_up_tile<P, 3, true>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 7: return gate_up_tile<P, 2, true>(a, tj, lds, rows, zc0, zw, rbase, k);
+        case 6: return gate_up_tile<P, 1, true>(a, tj, lds, rows, zc0, zw, rbase, k);
+        default: return gate_up_tile<P, 0, true>(a, tj, lds, rows, zc0, zw, rbase, k);
     }
 }
 
@@ -549,8 +544,9 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
         const int q = it * P::NT + tid;
         const int row = q / CHUNKS, c8 = (q % CHUNKS) * 8;
         if (row < tj.nrows && c8 < ncols) {
-            const uint4 v = *(const uint4 *)(st + stage_offset<P>(row, c8));
-            *(uint4 *)(yh + (size_t)rdst[row] * a.d + n0 + c8) = v;
+            // read by the combine only, after this launch: not kept in cache
+            const u32x4 v = *(const u32x4 *)(st + stage_offset<P>(row, c8));
+            __builtin_nontemporal_store(v, (u32x4 *)(yh + (size_t)rdst[row] * a.d + n0 + c8));
         }
     }
     return publish_item<P>(lds, a, k, ticket);
@@ -592,18 +588,17 @@ __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj
     // a split tile reads each W2 tile twice in a row (once per half), the
     // second time from L2: it keeps the default policy
     const bool stream_b = streams_weights(tj) && !split;
-    switch (wave_frags<P>(tj.nrows)) {
+    switch (wave_frags<P>(tj.nrows) + (stream_b ? 5 : 0)) {
         case 4: return down_tile<P, 4, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
         case 3: return down_tile<P, 3, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
         case 2: return down_tile<P, 2, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 1:
-            return stream_b
-                       ? down_tile<P, 1, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k)
-                       : down_tile<P, 1, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        default:
-            return stream_b
-                       ? down_tile<P, 0, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k)
-                       : down_tile<P, 0, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 1: return down_tile<P, 1, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 0: return down_tile<P, 0, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 9: return down_tile<P, 4, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 8: return down_tile<P, 3, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 7: return down_tile<P, 2, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 6: return down_tile<P, 1, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        default: return down_tile<P, 0, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
     }
 }
 

@@ -204,6 +204,27 @@ def graph_step_ms(layer, steps: int) -> float:
     return (time.perf_counter() - t0) * 1000.0 / steps
 
 
+def cold_step_ms(layer, steps: int) -> float:
+    """Median ms of one step timed alone with HIP events on torch's stream
+    (where the binding launches), each after writing a 512 MiB buffer, so
+    that neither L2 nor the 256 MB Infinity Cache still holds the previous
+    step's inputs or weights.  Reported beside the back-to-back step."""
+    import statistics
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        e0.record()
+        layer.step()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    return statistics.median(times)
+
+
 def cpu_baseline(layer, target_s: float):
     """The CPU oracle (as it stands) on the first S tokens of the same
     workload: router logits, routing and the layer output, double precision."""
@@ -631,6 +652,7 @@ def main(argv=None):
     stages = B.profile_collect()
     ms = (t1 - t0) * 1000.0 / args.steps
     graph_ms = None if args.no_graph else graph_step_ms(layer, args.steps)
+    cold_ms = cold_step_ms(layer, args.steps)
 
     counts = layer.route_out["counts"].cpu()
     touched = int((counts > 0).sum())
@@ -687,6 +709,7 @@ def main(argv=None):
                   "max_over_mean_load": float(counts.max()) / max(float(counts.float().mean()), 1e-9)},
         "stages_ms": stage_ms,
         "graph_ms_per_step": graph_ms,
+        "cold_cache_ms_per_step": cold_ms,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

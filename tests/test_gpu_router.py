@@ -25,6 +25,10 @@ CASES = {
     "v3_decode": CONFIGS["v3_decode"],
     # 384 experts: a second, half-empty column tile
     "v4_skew": CONFIGS["v4_skew"],
+    # 64 experts (softmax, one per lane): a mostly empty column tile
+    "mid": CONFIGS["mid"],
+    # 385 experts: a second column tile with 129 valid rows
+    "n385": scaled(CONFIGS["v3_prefill"], T=4096, d_model=512, d_ff=128).with_(n_routed=385),
     # a ragged row tile (333 = 256 + 77 tokens), two d ranges
     "ragged": scaled(CONFIGS["v3_prefill"], T=333, d_model=1024, d_ff=128),
     # d of 4 k-tiles: no split

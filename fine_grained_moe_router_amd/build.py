@@ -61,6 +61,27 @@ def build(verbose: bool = False, out: Path = LIB) -> Path:
     return out
 
 
+CALLER_SRC = ROOT / "tests" / "c_caller" / "moe_c_caller.c"
+CALLER = PKG / "moe_c_caller"
+ROCM = Path(os.environ.get("ROCM_PATH", "/opt/rocm"))
+
+
+def build_c_caller(verbose: bool = False, out: Path = CALLER) -> Path:
+    """Compile the C program that drives the library through include/moe.h
+    (a plain C11 host program: gcc, the HIP runtime's C API, libmoe.so)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-D__HIP_PLATFORM_AMD__", "-isystem", str(ROCM / "include"), f"-I{INCLUDE}",
+           str(CALLER_SRC), f"-L{PKG}", "-lmoe", f"-L{ROCM / 'lib'}", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM / 'lib'}", "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {CALLER_SRC.name}:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_caller(verbose=True)
     sys.exit(0)

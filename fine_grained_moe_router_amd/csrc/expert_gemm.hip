@@ -100,15 +100,16 @@ __device__ __forceinline__ TileRange tile_range(int total) {
 // tile start together, and its 16 (gate/up) or 28 (down) column tiles take
 // at most one XCD's worth of blocks.  A longer group (the shared experts, a
 // Zipf-hot expert with up to 25 row tiles at the V4 shape) is listed in
-// panels of kPanelRows row tiles x kPanelCols column tiles, 32 items, the
-// blocks of one XCD: a panel's blocks share 4 token-row tiles and 8 weight
-// tiles through the XCD's L2, 12 distinct operand tiles per k-step against
-// 18 for the same 32 items taken column tile fastest (2 row tiles x 16
-// column tiles), and a weight tile is streamed once per 4 row tiles instead
-// of once per row tile.  Interleaved A/B against column-fastest order: V4
-// skew gate/up -4.3%, down -3%; V3 prefill gate/up -0.8%.
+// panels of kPanelRows row tiles x kPanelCols column tiles, 64 items, two
+// rounds of one XCD's blocks: the blocks that run together share a few
+// token-row tiles and weight tiles through the XCD's L2, and a weight tile
+// is streamed once per 8 row tiles instead of once per row tile.
+// Interleaved A/B: 4 x 8 panels against column-fastest order, V4 skew
+// gate/up -4.3%, down -3%, V3 prefill gate/up -0.8%; then 8 x 8 against
+// 4 x 8, gate/up -1% (V4 skew, V3 prefill) and -3% (the 16B shape's shared
+// experts), down within noise.
 constexpr int kColMajorRows = 4;
-constexpr int kPanelRows = 4, kPanelCols = 8;
+constexpr int kPanelRows = 8, kPanelCols = 8;
 
 struct XcdQueue {
     int m0, ms, m1, ntr, nts, nr_items, total;

@@ -292,6 +292,10 @@ int forward_impl(const moe_config &c, const void *x, const int32_t *topk_idx, co
     a.ys = (float *)(ws + L.off_ys);
     a.yrh = (uint16_t *)(ws + L.off_yrh);
     a.ysh = (uint16_t *)(ws + L.off_ysh);
+    a.shared_f16 = shared_f16(c) ? 1 : 0;
+    a.zs16 = (uint16_t *)(ws + L.off_zs16);
+    a.w2s16 = (const uint16_t *)(ws + L.off_w2s16);
+    a.f16bad = (int32_t *)meta + mi.f16bad;
     {
         StageScope sc(MOE_STAGE_GATE_UP, s);
         a.tile_base = meta + mi.tile1;

@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kXcds = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
@@ -93,6 +94,8 @@ struct FwdLayout {
     size_t off_ys;      // fp32 [T][d]: summed shared-expert outputs
     size_t off_yrh;     // bf16 layers: fp16 copies of the two above, read by
     size_t off_ysh;     //   the combine (fp32 only where fp16 overflows)
+    size_t off_zs16;    // shared_f16: fp16 [T][K_s*d_ff_shared], z of the shared group
+    size_t off_w2s16;   // shared_f16: fp16 [K_s][d][d_ff_shared], the shared W2
     size_t total;
 };
 
@@ -105,7 +108,7 @@ struct FwdLayout {
 //   bad                              count of out-of-range expert ids
 // q1, q2 and bad start at zero (set by the permutation).
 struct MetaIdx {
-    int group_off, group_cnt, tile1, tile2, mt, xs1, xs2, q1, q2, bad, size;
+    int group_off, group_cnt, tile1, tile2, mt, xs1, xs2, q1, q2, bad, f16bad, size;
 };
 __host__ __device__ inline MetaIdx meta_index(int G) {
     MetaIdx m;
@@ -119,7 +122,8 @@ __host__ __device__ inline MetaIdx meta_index(int G) {
     m.q1 = 5 * G + 23;
     m.q2 = 5 * G + 31;
     m.bad = 5 * G + 39;
-    m.size = 5 * G + 40;
+    m.f16bad = 5 * G + 40;
+    m.size = 5 * G + 41;
     return m;
 }
 
@@ -158,6 +162,14 @@ struct GroupedArgs {
     void *zr, *zs;
     float *yr, *ys;
     uint16_t *yrh, *ysh;      // fp16 outputs of the bf16 kernels (see f16x4_value)
+    // The shared experts' fp16 down pass (shared_f16): z as one fp16 plane,
+    // W2 of the shared experts converted to fp16, and the flag either
+    // conversion sets when fp16 cannot hold a value (the down launch then
+    // takes the (hi, lo) pass)
+    int shared_f16;
+    uint16_t *zs16;
+    const uint16_t *w2s16;
+    int32_t *f16bad;
 };
 
 // ---- launchers (each returns hipSuccess or the launch error) ---------------
@@ -199,6 +211,14 @@ int select_blocks(const moe_config &c);   // blocks of the select kernel
 // reach h unscaled.
 inline bool z_split_shared(const moe_config &c) { return c.dtype == MOE_BF16 && c.n_shared > 0; }
 inline bool z_split_routed(const moe_config &c) { return c.dtype == MOE_BF16 && c.top_k == 1; }
+// The shared group's down projection in fp16 instead of the (hi, lo) pass:
+// z rounded once to fp16 (11 significant bits, 8 times bf16's precision)
+// against W2 converted to fp16, which halves the shared group's down work.
+// Used where the shared group has more than 128 rows (fewer: the folded
+// (hi, lo) tile below), as long as fp16 holds every value of z and W2.
+inline bool shared_f16(const moe_config &c) {
+    return c.dtype == MOE_BF16 && c.n_shared > 0 && c.T > 128;
+}
 
 FwdLayout fwd_layout(const moe_config &c);
 TileShape tile_shape(const moe_config &c);

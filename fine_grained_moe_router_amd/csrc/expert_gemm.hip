@@ -331,6 +331,20 @@ __device__ __forceinline__ int gate_up_tile(const GroupedArgs &a, const TileJob 
                         lo[3] = z[3] - bf16_to_f32((uint16_t)(hi.y >> 16));
                         *(uint2 *)(dst + zw) = pack_bf16x4(lo);
                     }
+                    if (tj.shared && a.shared_f16) {
+                        // z once more as fp16, for the shared group's fp16
+                        // down pass; a value fp16 cannot hold flags it off
+                        uint16_t h[4];
+                        bool over = false;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            over |= !(fabsf(z[q]) < 65520.0f);
+                            h[q] = __builtin_bit_cast(uint16_t, (_Float16)z[q]);
+                        }
+                        *(uint2 *)(a.zs16 + (rbase + row) * zw + col) =
+                            make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                        if (over) atomicOr(a.f16bad, 1);
+                    }
                 }
             }
             // keep one fragment pair live at a time
@@ -442,16 +456,41 @@ __device__ __forceinline__ int stage_offset(int row, int col) {
 // the tile staged in LDS (the A stages and the first two B stages), then
 // each wave stores two whole rows of 512 bytes at a time with 16-byte lane
 // stores.  A value beyond fp16's range (rare) is also stored as fp32.
-template <class P, int NF, bool STREAM_B>
+//
+// FOLD: a split tile of at most 128 rows whose lo plane sits in the tile's
+// rows 128-255 (row 128 + r holds lo of row r; see down_body): each W2
+// k-range is read once for both planes, the wave computes its hi fragments
+// i < NF and their lo partners i + 2, and y = hi part + lo part is added in
+// fp32 before the epilogue.
+//
+// F16: the shared group's fp16 pass (z's fp16 plane against the fp16 copy
+// of the shared W2, K = K_s d_ff_s).
+template <class P, int NF, bool STREAM_B, bool FOLD, bool F16 = false>
 __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj, char *lds,
                                          const OperandRows<P> &rows, int K, int split, int n0,
                                          int my_pair, float my_gate, int k) {
-    f32x16 acc[NF > 0 ? NF : 1][P::FN];
-    if (tj.shared)
+    constexpr int NP = (FOLD && NF > 0) ? NF + 2 : NF;   // fragments the K loop spans
+    constexpr int FMASK = FOLD ? ((1 << NF) - 1) * 5 : (1 << NP) - 1;
+    f32x16 acc[NP > 0 ? NP : 1][P::FN];
+    if constexpr (F16) {
+        pipe_gemm_nf<P, false, NF, true, false, (1 << NF) - 1, true>(
+            lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, 0, acc);
+    } else if constexpr (FOLD) {
+        if (tj.shared)
+            pipe_gemm_nf<P, false, NP, false, STREAM_B, FMASK>(lds, rows, K, a.fs, a.n_shared,
+                                                               (size_t)a.d * a.fs, 0, acc);
+        else
+            pipe_gemm_nf<P, false, NP, false, STREAM_B, FMASK>(lds, rows, K, 0, 1, 0, 0, acc);
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+#pragma unroll
+            for (int j = 0; j < P::FN; ++j) acc[i][j] += acc[i + 2][j];
+    } else if (tj.shared) {
         pipe_gemm_nf<P, false, NF, true, STREAM_B>(lds, rows, K, a.fs, a.n_shared,
                                                    (size_t)a.d * a.fs, split ? K / 2 : 0, acc);
-    else
+    } else {
         pipe_gemm_nf<P, false, NF, true, STREAM_B>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
+    }
     int32_t *rdst = (int32_t *)(lds + tile_info_offset<P>());   // destination row
     float *rgate = (float *)(lds + tile_info_offset<P>() + 4 * P::BM);
     if (threadIdx.x < P::BM) {
@@ -555,57 +594,116 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
 
 template <class P>
 __device__ __forceinline__ int down_body(const GroupedArgs &a, const TileJob &tj, char *lds,
-                                         int k) {
+                                         int k, bool f16) {
     const int fsum = a.n_shared * a.fs;
     const int n0 = tj.j * P::BN;
     const int goff = tj.goff;
     // K runs over z, or over (hi, lo) of a split group: the two halves of
     // each 64-wide k-range back to back, so W2 streams once
     const int split = tj.shared ? a.split_s : a.split_r;
-    const int K = (tj.shared ? fsum : a.f) * (split ? 2 : 1);
+    const int Kh = tj.shared ? fsum : a.f;   // z's width (one plane)
+    const int K = Kh * (split ? 2 : 1);
     const size_t rbase = tj.shared ? (size_t)tj.row0 : (size_t)goff + tj.row0;
-    // Both operands are affine: z rows rbase.. and W2 rows n0.. (z rows past
-    // the group are not fetched; W2 rows past d fetch row d - 1).
-    OperandRows<P> rows;
-    rows.abase = (const uint16_t *)(tj.shared ? a.zs : a.zr) + rbase * K;
-    const int r0 = P::load_row(threadIdx.x, 0);
-    rows.aoff[0] = (uint32_t)r0 * (uint32_t)K;
-    rows.astep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)K;
-    rows.amask = valid_row_mask<P>(tj.nrows);
-    rows.azero = pad_row_mask<P>(tj.nrows);
     const int wk = tj.shared ? a.fs : a.f;   // row length of the W2 matrix
-    rows.bbase = tj.shared ? (const uint16_t *)a.w2s
-                           : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
-    rows.boff[0] = (uint32_t)(n0 + r0) * (uint32_t)wk;
-    rows.bstep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)wk;
-    rows.bmask = valid_row_mask<P>(a.d - n0);
-    rows.blast = (uint32_t)(a.d - 1) * (uint32_t)wk;
+    const uint16_t *zbase = (const uint16_t *)(tj.shared ? a.zs : a.zr) + rbase * K;
+    const uint16_t *w2base = tj.shared ? (const uint16_t *)a.w2s
+                                       : (const uint16_t *)a.w2 + (size_t)tj.g * a.d * a.f;
+    const int r0 = P::load_row(threadIdx.x, 0);
     int my_pair = 0;
     float my_gate = 0.0f;
     if (!tj.shared && (int)threadIdx.x < tj.nrows) {
         my_pair = a.perm[rbase + threadIdx.x];
         my_gate = a.gsort[rbase + threadIdx.x];
     }
+    OperandRows<P> rows;
+    rows.abase = zbase;
+    rows.bbase = w2base;
+    if (tj.shared && f16) {
+        // fp16 pass: z rows rbase.. of the fp16 plane (K = K_s d_ff_s) and
+        // the fp16 shared W2, both affine as below
+        rows.abase = a.zs16 + rbase * fsum;
+        rows.bbase = a.w2s16;
+        rows.aoff[0] = (uint32_t)r0 * (uint32_t)fsum;
+        rows.astep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)fsum;
+        rows.amask = valid_row_mask<P>(tj.nrows);
+        rows.azero = pad_row_mask<P>(tj.nrows);
+        rows.boff[0] = (uint32_t)(n0 + r0) * (uint32_t)wk;
+        rows.bstep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)wk;
+        rows.bmask = valid_row_mask<P>(a.d - n0);
+        rows.blast = (uint32_t)(a.d - 1) * (uint32_t)wk;
+        switch (wave_frags<P>(tj.nrows)) {
+            case 4: return down_tile<P, 4, false, false, true>(a, tj, lds, rows, fsum, 0, n0, my_pair, my_gate, k);
+            case 3: return down_tile<P, 3, false, false, true>(a, tj, lds, rows, fsum, 0, n0, my_pair, my_gate, k);
+            case 2: return down_tile<P, 2, false, false, true>(a, tj, lds, rows, fsum, 0, n0, my_pair, my_gate, k);
+            case 1: return down_tile<P, 1, false, false, true>(a, tj, lds, rows, fsum, 0, n0, my_pair, my_gate, k);
+            default: return down_tile<P, 0, false, false, true>(a, tj, lds, rows, fsum, 0, n0, my_pair, my_gate, k);
+        }
+    }
+    if (split && tj.nrows <= P::BM / 2) {
+        // Folded split tile (few rows: a hash-routed expert, a decode-sized
+        // shared group): tile row r < 128 fetches the hi plane of z row r,
+        // tile row 128 + r its lo plane, so one pass over the W2 k-ranges
+        // serves both (K = one plane) instead of reading every W2 tile twice
+        // over twice the k-tiles.  Per-load offsets: not affine across the
+        // two halves.
+        const int pad = min(P::BM / 2, (tj.nrows + 31) & ~31);
+        uint32_t amask = 0, azero = 0;
+#pragma unroll
+        for (int n = 0; n < P::A_LD; ++n) {
+            const int row = P::load_row(threadIdx.x, n);
+            const int zr = row & (P::BM / 2 - 1);
+            rows.aoff[n] = (uint32_t)zr * (uint32_t)K + (row >= P::BM / 2 ? (uint32_t)Kh : 0u);
+            amask |= (zr < tj.nrows ? 1u : 0u) << n;
+            azero |= (zr >= tj.nrows && zr < pad ? 1u : 0u) << n;
+        }
+#pragma unroll
+        for (int n = 0; n < P::B_LD; ++n)
+            rows.boff[n] = (uint32_t)min(n0 + P::load_row(threadIdx.x, n), a.d - 1) * (uint32_t)wk;
+        rows.amask = amask;
+        rows.azero = azero;
+        const bool stream_b = streams_weights(tj);
+        switch (wave_frags<P>(tj.nrows) + (stream_b ? 3 : 0)) {
+            case 2: return down_tile<P, 2, false, true>(a, tj, lds, rows, Kh, split, n0, my_pair, my_gate, k);
+            case 1: return down_tile<P, 1, false, true>(a, tj, lds, rows, Kh, split, n0, my_pair, my_gate, k);
+            case 0: return down_tile<P, 0, false, true>(a, tj, lds, rows, Kh, split, n0, my_pair, my_gate, k);
+            case 5: return down_tile<P, 2, true, true>(a, tj, lds, rows, Kh, split, n0, my_pair, my_gate, k);
+            case 4: return down_tile<P, 1, true, true>(a, tj, lds, rows, Kh, split, n0, my_pair, my_gate, k);
+            default: return down_tile<P, 0, true, true>(a, tj, lds, rows, Kh, split, n0, my_pair, my_gate, k);
+        }
+    }
+    // Both operands are affine: z rows rbase.. and W2 rows n0.. (z rows past
+    // the group are not fetched; W2 rows past d fetch row d - 1).
+    rows.aoff[0] = (uint32_t)r0 * (uint32_t)K;
+    rows.astep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)K;
+    rows.amask = valid_row_mask<P>(tj.nrows);
+    rows.azero = pad_row_mask<P>(tj.nrows);
+    rows.boff[0] = (uint32_t)(n0 + r0) * (uint32_t)wk;
+    rows.bstep = (uint32_t)(P::NT / P::CHUNKS) * (uint32_t)wk;
+    rows.bmask = valid_row_mask<P>(a.d - n0);
+    rows.blast = (uint32_t)(a.d - 1) * (uint32_t)wk;
     // a split tile reads each W2 tile twice in a row (once per half), the
     // second time from L2: it keeps the default policy
     const bool stream_b = streams_weights(tj) && !split;
     switch (wave_frags<P>(tj.nrows) + (stream_b ? 5 : 0)) {
-        case 4: return down_tile<P, 4, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 3: return down_tile<P, 3, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 2: return down_tile<P, 2, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 1: return down_tile<P, 1, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 0: return down_tile<P, 0, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 9: return down_tile<P, 4, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 8: return down_tile<P, 3, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 7: return down_tile<P, 2, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        case 6: return down_tile<P, 1, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
-        default: return down_tile<P, 0, true>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 4: return down_tile<P, 4, false, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 3: return down_tile<P, 3, false, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 2: return down_tile<P, 2, false, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 1: return down_tile<P, 1, false, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 0: return down_tile<P, 0, false, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 9: return down_tile<P, 4, true, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 8: return down_tile<P, 3, true, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 7: return down_tile<P, 2, true, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        case 6: return down_tile<P, 1, true, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
+        default: return down_tile<P, 0, true, false>(a, tj, lds, rows, K, split, n0, my_pair, my_gate, k);
     }
 }
 
 template <class P>
 __global__ __launch_bounds__(P::NT) void k_down_bf16(const GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[P::LDS_BYTES];
+    // the shared group's fp16 pass, unless fp16 could not hold a value of z
+    // or of the shared W2 (flag set by the gate/up launch or the conversion)
+    const bool f16 = a.shared_f16 && __builtin_amdgcn_readfirstlane(a.f16bad[0]) == 0;
     int item = first_item<P>(lds, a);
     while (item >= 0) {
         int m, j;
@@ -613,8 +711,33 @@ __global__ __launch_bounds__(P::NT) void k_down_bf16(const GroupedArgs a) {
         item_tile(a, item, m, j, d);
         TileJob tj = row_tile(a, d, m, P::BM);
         tj.j = j;
-        item = down_body<P>(a, tj, lds, queue_step(item));
+        item = down_body<P>(a, tj, lds, queue_step(item), f16);
     }
+}
+
+// The shared experts' W2 as fp16, for the shared group's fp16 down pass.  A
+// bf16 value in fp16's normal range converts exactly (its 8 significant bits
+// fit fp16's 11); below it, bits under 2^-24 are lost; a value fp16 cannot
+// hold (|w| >= 65520, or not finite) sets the flag, and the down launch
+// takes the (hi, lo) pass instead.
+__global__ __launch_bounds__(256) void k_shared_w2_f16(size_t n4, const uint2 *__restrict__ src,
+                                                       uint2 *__restrict__ dst,
+                                                       int32_t *__restrict__ bad) {
+    bool over = false;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const uint2 v = src[i];
+        const float f[4] = {bf16_to_f32((uint16_t)(v.x & 0xFFFF)), bf16_to_f32((uint16_t)(v.x >> 16)),
+                            bf16_to_f32((uint16_t)(v.y & 0xFFFF)), bf16_to_f32((uint16_t)(v.y >> 16))};
+        uint16_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            over |= !(fabsf(f[q]) < 65520.0f);
+            h[q] = __builtin_bit_cast(uint16_t, (_Float16)f[q]);
+        }
+        dst[i] = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    }
+    if (over) atomicOr(bad, 1);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT
@@ -764,6 +887,11 @@ hipError_t launch_down(const moe_config &c, const GroupedArgs &a0, hipStream_t s
     if (c.dtype == MOE_BF16) {
         const int grid = persistent_grid(1ll << 30, 1);
         GroupedArgs a = a0;
+        if (a.shared_f16) {
+            const size_t n = (size_t)c.n_shared * c.d_model * c.d_ff_shared;
+            hipLaunchKernelGGL(k_shared_w2_f16, dim3(1024), dim3(256), 0, s, n / 4,
+                               (const uint2 *)a.w2s, (uint2 *)a.w2s16, a.f16bad);
+        }
         a.nt_routed = a.nt_shared = (c.d_model + ts.bn2 - 1) / ts.bn2;
         hipLaunchKernelGGL(k_down_bf16<PipeTile>, dim3(grid), dim3(PipeTile::NT), 0, s, a);
     } else {

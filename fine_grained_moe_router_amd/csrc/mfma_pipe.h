@@ -169,8 +169,12 @@ __device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byt
 // ((k0 / bsplit) % bmod) * bstride + k0 % bsplit (B made of several matrices
 // side by side along K, possibly repeated).  AFF: both operands are affine
 // (rows.aoff[0], rows.astep; rows.boff[0], rows.bstep).  STREAM_B: B is
-// read by this tile alone and once, so its loads are non-temporal.
-template <class P, bool SPLIT, int NF, bool AFF = false, bool STREAM_B = false>
+// read by this tile alone and once, so its loads are non-temporal.  FMASK:
+// which of the NF leading fragments the wave computes (all by default; a
+// folded split tile skips the fragments between its hi and lo rows).  F16:
+// both operands are fp16 (v_mfma_f32_32x32x16_f16) instead of bf16.
+template <class P, bool SPLIT, int NF, bool AFF = false, bool STREAM_B = false,
+          int FMASK = (1 << NF) - 1, bool F16 = false>
 __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &rows, int K,
                                              int bsplit, int bmod, size_t bstride, int a_half,
                                              f32x16 (&acc)[NF > 0 ? NF : 1][P::FN]) {
@@ -302,19 +306,21 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
         const uint32_t sb_next = b_cur == 0 ? 2u * P::B_STAGE : b_cur - P::B_STAGE;
         const char *Ab = a_lds + a_cur;
         const char *Bb = b_lds + b_cur;
-        bf16x8 a[2][NA], b[2][P::FN];
-        auto frag_load = [&](int s, bf16x8 (&av)[NA], bf16x8 (&bv)[P::FN]) {
+        using V8 = std::conditional_t<F16, f16x8, bf16x8>;
+        V8 a[2][NA], b[2][P::FN];
+        auto frag_load = [&](int s, V8 (&av)[NA], V8 (&bv)[P::FN]) {
             const char *As = Ab + lofs[s];
             const char *Bs = Bb + lofs[s];
 #pragma unroll
             for (int j = 0; j < P::FN; ++j) {
                 const int row0 = P::template b_row<SPLIT>(wn, j);   // a multiple of 32
-                bv[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Bs + row0 * P::CHUNKS * 16));
+                bv[j] = __builtin_bit_cast(V8, *(const u32x4 *)(Bs + row0 * P::CHUNKS * 16));
             }
 #pragma unroll
             for (int i = 0; i < NF; ++i) {
+                if (!((FMASK >> i) & 1)) continue;
                 const int row0 = P::a_row(wm, i);
-                av[i] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(As + row0 * P::CHUNKS * 16));
+                av[i] = __builtin_bit_cast(V8, *(const u32x4 *)(As + row0 * P::CHUNKS * 16));
             }
         };
         frag_load(0, a[0], b[0]);
@@ -326,11 +332,15 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
             for (int q = 0; q < GROUPS; ++q) {
 #pragma unroll
                 for (int i = 0; i < NF; ++i)
-                    if (i == q)
+                    if (i == q && ((FMASK >> i) & 1))
 #pragma unroll
                         for (int j = 0; j < P::FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+                            if constexpr (F16)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+                            else
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
                 // this group's share of the next loads, A loads first, then B
 #pragma unroll
                 for (int n = 0; n < LOADS; ++n) {

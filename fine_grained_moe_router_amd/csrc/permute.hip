@@ -62,6 +62,11 @@ FwdLayout fwd_layout(const moe_config &c) {
     o = align256(o + P * c.d_model * hb);
     L.off_ysh = o;
     o = align256(o + (size_t)(c.n_shared > 0 ? c.T : 0) * c.d_model * hb);
+    const bool f16 = shared_f16(c);
+    L.off_zs16 = o;
+    o = align256(o + (f16 ? (size_t)c.T * c.n_shared * c.d_ff_shared * 2 : 0));
+    L.off_w2s16 = o;
+    o = align256(o + (f16 ? (size_t)c.n_shared * c.d_model * c.d_ff_shared * 2 : 0));
     L.total = o;
     return L;
 }
@@ -322,7 +327,7 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
     int32_t *cc = (int32_t *)(ws + L.off_chunk);
     int32_t *meta = (int32_t *)(ws + L.off_meta);
     const MetaIdx mi = meta_index(L.G);
-    hipError_t e = launch_fill_i32(meta + mi.q1, mi.bad + 1 - mi.q1, 0, s);   // q1, q2, bad
+    hipError_t e = launch_fill_i32(meta + mi.q1, mi.f16bad + 1 - mi.q1, 0, s);   // q1, q2, bad, f16bad
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_perm_hist, dim3(L.n_chunks), dim3(256), (size_t)N * 4, s, P, N, L.chunk,
                        idx, cc, meta + mi.bad);
@@ -330,7 +335,9 @@ hipError_t launch_permute(const moe_config &c, const FwdLayout &L, const int32_t
                        meta + mi.group_cnt);
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, N, c.T, c.n_shared, c.d_ff,
                        c.n_shared * c.d_ff_shared, c.d_model, z_split_routed(c) ? 1 : 0,
-                       z_split_shared(c) ? 1 : 0, tile_shape(c), meta, (RowTileDesc *)(ws + L.off_rtd));
+                       // the shared group's down K: one fp16 pass, or the (hi, lo) pair
+                       (z_split_shared(c) && !shared_f16(c)) ? 1 : 0, tile_shape(c), meta,
+                       (RowTileDesc *)(ws + L.off_rtd));
     hipLaunchKernelGGL(k_perm_scatter, dim3(L.n_chunks), dim3(64), (size_t)N * 4, s, P, N,
                        L.chunk, idx, topk_w, cc, meta + mi.group_off, (int32_t *)(ws + L.off_perm),
                        (float *)(ws + L.off_gsort));

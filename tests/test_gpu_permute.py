@@ -34,7 +34,7 @@ def layout(T, K, N, n_shared):
     n_chunks = -(-P // chunk)
     G = N + (1 if n_shared else 0)
     off_meta = align256(n_chunks * N * 4)
-    off_perm = align256(off_meta + (5 * G + 40) * 4)
+    off_perm = align256(off_meta + (5 * G + 41) * 4)
     off_gsort = align256(off_perm + P * 4)
     return chunk, n_chunks, off_meta, off_perm, off_gsort
 
@@ -92,7 +92,7 @@ def test_permutation_is_the_stable_sort(name):
     perm = w[off_perm:off_perm + 4 * P].view(np.int32)
     gsort = w[off_gsort:off_gsort + 4 * P].view(np.uint32)
     G = N + (1 if cfg.n_shared else 0)
-    meta = w[off_meta:off_meta + 4 * (5 * G + 40)].view(np.int32)
+    meta = w[off_meta:off_meta + 4 * (5 * G + 41)].view(np.int32)
 
     ids = idx.ravel()
     valid = (ids >= 0) & (ids < N)

@@ -177,7 +177,10 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_gate,
  * computed once (dropless).  The result is bitwise reproducible run to run.
  * Arithmetic: bf16 products with fp32 accumulation; the SwiGLU hidden
  * activation is rounded to the input dtype before the down projection (for
- * gate-1 groups with bf16, to a pair of bf16 values); with bf16, each
+ * gate-1 groups with bf16, to a pair of bf16 values; for the shared experts
+ * of a batch of more than 128 tokens, to fp16, their down projection then
+ * running on fp16 products against W2 converted to fp16 -- or on the bf16
+ * pair when fp16 cannot hold a value of z or of that W2); with bf16, each
  * gate-scaled expert output is held as fp16 until the sum (as fp32 where it
  * exceeds fp16's range); the sum is formed in fp32 and rounded once
  * (nearest-even) into h.

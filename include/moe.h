@@ -215,7 +215,7 @@ int moe_forward(const moe_config *cfg, const void *x, const int32_t *topk_idx,
  * nothing (no hipMalloc, hipFree or allocating library routine).
  *  - Configs whose moe_workspace_bytes(cfg, MOE_WS_FORWARD) exceeds
  *    MOE_STATIC_SCRATCH_BYTES return MOE_ERR_UNSUPPORTED (at the V3 layer
- *    shape, batches of up to about 150 tokens fit: decode-sized work).
+ *    shape, batches of up to 128 tokens fit: decode-sized work).
  *  - Every call on one GPU shares that GPU's array and leaves its contents
  *    behind; nothing in it needs to start at zero (the call clears what its
  *    kernels count from).  Calls that overlap on one GPU -- on different

@@ -2,9 +2,10 @@
 
 * Batch sizes around the implementation's switches at the V3 layer shape
   (d = 7168, 256 routed top-8 + 1 shared): T = 1 (one token, thin tiles
-  everywhere), 4095 / 4096 / 4097 (the select kernel takes two tokens per
-  wave from 4096 on, and the router's d split and the row-tile counts
-  change with T).
+  everywhere), 128 / 129 (the shared group's down pass folds its bf16 pair
+  into one tile up to 128 rows, and runs in fp16 beyond), 4095 / 4096 /
+  4097 (the select kernel takes two tokens per wave from 4096 on, and the
+  router's d split and the row-tile counts change with T).
 * The largest batch the API takes: T K' = 2^22 pairs (T = 524,288, K' = 8,
   d = 256), the permutation's largest chunks and ~16k row tiles per GEMM.
 * Node-limited routing at the full V4 shape on the V4 book's layout (384
@@ -52,7 +53,7 @@ def check_layer(cfg, inp, r, tokens):
           flush=True)
 
 
-@pytest.mark.parametrize("T", [1, 4095, 4096, 4097])
+@pytest.mark.parametrize("T", [1, 128, 129, 4095, 4096, 4097])
 def test_v3_batch_size_edges(T):
     cfg = CONFIGS["v3_prefill"].with_(name=f"v3_T{T}", T=T)
     print(f"[edges] {cfg.name}", flush=True)

@@ -29,10 +29,12 @@ def route_and_compare(cfg, inp, T):
     assert torch.equal(ref.view(torch.uint8), got.view(torch.uint8)), (cfg.name, T)
 
 
-@pytest.mark.parametrize("name", ["v3_decode", "toy_fp32", "hash_small"])
+@pytest.mark.parametrize("name", ["v3_decode", "v3_128", "toy_fp32", "hash_small"])
 def test_forward_static_matches_forward(name):
     if name == "hash_small":
         cfg = scaled(CONFIGS["v4_hash"], T=256, d_model=512, d_ff=256)
+    elif name == "v3_128":   # the largest V3 batch the scratch holds
+        cfg = CONFIGS["v3_decode"].with_(name="v3_128", T=128)
     else:
         cfg = CONFIGS[name]
     inp = make_inputs(cfg, "cuda")

@@ -148,3 +148,23 @@ def check_routing_identical_logits(cfg, inp, r):
         np.testing.assert_allclose(to_numpy(r["P"]), P, rtol=1e-6, atol=1e-12)
         np.testing.assert_allclose(to_numpy(r["loss"]), loss, rtol=1e-6)
     return idx, gate
+
+
+def align256(v):
+    return (v + 255) & ~255
+
+
+def forward_workspace_layout(T, K, N, n_shared):
+    """Offsets into moe_forward's workspace, restating the library's layout
+    (per-chunk counts, the metadata block of 5 G + 41 ints, then the pair ids
+    and the gates, each 256-byte aligned): (pair chunk, chunks, offset of the
+    metadata, of the pair ids, of the gates).  A change of that layout must
+    be made here too."""
+    P = T * K
+    chunk = max(64, -(-(-(-P // 256)) // 64) * 64)
+    n_chunks = -(-P // chunk)
+    G = N + (1 if n_shared else 0)
+    off_meta = align256(n_chunks * N * 4)
+    off_perm = align256(off_meta + (5 * G + 41) * 4)
+    off_gsort = align256(off_perm + P * 4)
+    return chunk, n_chunks, off_meta, off_perm, off_gsort

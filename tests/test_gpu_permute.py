@@ -20,23 +20,9 @@ from fine_grained_moe_router_amd import binding as B
 from fine_grained_moe_router_amd.configs import CONFIGS, scaled
 from fine_grained_moe_router_amd.synth import make_inputs, make_share_routing
 
+from parity import forward_workspace_layout as layout
+
 pytestmark = pytest.mark.gpu
-
-
-def align256(v):
-    return (v + 255) & ~255
-
-
-def layout(T, K, N, n_shared):
-    """(pair chunk, chunks, offset of the metadata, of the pair ids, of the gates)."""
-    P = T * K
-    chunk = max(64, -(-(-(-P // 256)) // 64) * 64)
-    n_chunks = -(-P // chunk)
-    G = N + (1 if n_shared else 0)
-    off_meta = align256(n_chunks * N * 4)
-    off_perm = align256(off_meta + (5 * G + 41) * 4)
-    off_gsort = align256(off_perm + P * 4)
-    return chunk, n_chunks, off_meta, off_perm, off_gsort
 
 
 def distinct_rows(rng, T, K, N):

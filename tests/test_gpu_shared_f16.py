@@ -4,10 +4,10 @@ Where the shared group has more than 128 rows, the down projection runs it
 in fp16: z rounded once to fp16 against the shared W2 converted to fp16.
 A value fp16 cannot hold (in z, or in the shared W2) sets a flag, and the
 down launch then runs the (hi, lo) bf16 pair instead.  These tests read the
-flag back from the forward workspace (its offset restates the workspace
-layout, as tests/test_gpu_permute.py does) and hold h to the oracle in every
-case: within the end-to-end tolerance for ordinary weights, and within the
-same error relative to the output's scale where weights are scaled up."""
+flag back from the forward workspace (parity.forward_workspace_layout) and
+hold h to the oracle in every case: within the end-to-end tolerance for
+ordinary weights, and within the same error relative to the output's scale
+where weights are scaled up."""
 import numpy as np
 import pytest
 import torch
@@ -16,8 +16,8 @@ from fine_grained_moe_router_amd import binding as B
 from fine_grained_moe_router_amd.configs import CONFIGS, scaled
 from fine_grained_moe_router_amd.synth import make_inputs
 
-from parity import check_routing_identical_logits, compare_h, gpu_h_as_f64, oracle_h
-from test_gpu_permute import layout
+from parity import (check_routing_identical_logits, compare_h, forward_workspace_layout,
+                    gpu_h_as_f64, oracle_h)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,8 @@ def layer_and_flag(cfg, inp):
     f, P, loss = B.balance_stats(cfg, r["counts"], r["pstat"])
     torch.cuda.synchronize()
     r.update(h=h, f=f, P=P, loss=loss)
-    _, _, off_meta, _, _ = layout(cfg.T, cfg.top_k, cfg.n_routed, cfg.n_shared)
+    _, _, off_meta, _, _ = forward_workspace_layout(cfg.T, cfg.top_k, cfg.n_routed,
+                                                    cfg.n_shared)
     G = cfg.n_routed + 1
     at = off_meta + 4 * (5 * G + 40)
     flag = int(ws[at:at + 4].cpu().view(torch.int32)[0])

@@ -46,6 +46,12 @@ SMALL = {
     # ~375 rows per routed expert and two 64-wide shared experts side by side
     "many_rows_two_shared": scaled(CONFIGS["mid"], T=1500, d_model=256, d_ff=128).with_(
         n_routed=8, top_k=2, n_shared=2, d_ff_shared=64),
+    # hash routing over 12 experts, ~240 rows each: routed (hi, lo) tiles of
+    # more than 128 rows take the unfolded pass, over one or two row tiles.
+    # At T = 3000 one output reaches |h| = 8.27, where bf16's half-ulp alone
+    # (0.031) exceeds the 2e-2 bar; T = 2900 keeps every |h| below 8 (6.76).
+    "hash_many_rows": scaled(CONFIGS["v4_hash"], T=2900, d_model=256, d_ff=128).with_(
+        n_routed=12),
 }
 
 

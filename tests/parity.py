@@ -56,7 +56,8 @@ def oracle_route_tokens(cfg: LayerConfig, inp: LayerInputs, tokens, x_h=None):
     x_h = host(inp.x) if x_h is None else x_h
     lg = O.router_logits(x_h, host(inp.w_gate), tokens=tokens)
     idx, gate, s32, gap = O.route(lg, cfg.n_routed, cfg.top_k, cfg.scoring, cfg.renorm,
-                                  offset=host(inp.offset), bias=host(inp.bias))
+                                  offset=host(inp.offset), bias=host(inp.bias),
+                                  n_groups=cfg.n_groups, topk_groups=cfg.topk_groups)
     return lg, idx, gate, s32, gap
 
 

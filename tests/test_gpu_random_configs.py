@@ -1,0 +1,69 @@
+"""Seeded random layer configurations against the oracle, end to end.
+
+Each case draws a small layer from the API's whole space: bf16 or fp32;
+1..400 tokens; d and d_ff from 64 to 512 / 256 (multiples of 64); 1..256
+routed experts with K' up to 16; 0..2 shared experts; softmax, sigmoid,
+sqrt(softplus) or hash scoring, with or without renormalisation, selection
+bias and a Zipf logit offset; and, for a third of the learned routings, a
+node limit.  The layer (moe_route, moe_forward, moe_balance_stats) is held
+to the same bar as the fixed cases: routing bit-exact on the GPU's logits,
+gates within 1 ulp, f bit-exact, P and the loss to 1e-6, and h within the
+dtype's tolerance of the oracle's layer on that same routing, every token
+(softmax over hundreds of experts leaves most tokens within 1e-4 of a tie,
+so the near-tie exclusion of the fixed cases would leave too few)."""
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_moe_router_amd.configs import LayerConfig
+from fine_grained_moe_router_amd.synth import make_inputs
+
+from parity import check_routing_identical_logits, compare_h, gpu_h_as_f64, gpu_layer, oracle_h
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def draw(i):
+    rng = np.random.default_rng(1000 + i)
+    dtype = "f32" if rng.random() < 0.2 else "bf16"
+    scoring = rng.choice(["softmax", "sigmoid", "sqrt_softplus", "hash"], p=[0.3, 0.3, 0.25, 0.15])
+    N = int(rng.choice([1, 2, 5, 8, 16, 33, 64, 100, 256]))
+    K = 1 if scoring == "hash" else int(rng.integers(1, min(N, 16) + 1))
+    n_shared = int(rng.integers(0, 3))
+    groups, topk_groups = 0, 0
+    if scoring != "hash" and rng.random() < 0.33:
+        divs = [g for g in range(2, min(N, 64) + 1) if N % g == 0]
+        if divs:
+            groups = int(rng.choice(divs))
+            need = -(-K // (N // groups))          # groups needed to hold K' experts
+            topk_groups = int(rng.integers(need, groups + 1))
+    return LayerConfig(
+        name=f"rand{i:02d}", T=int(rng.integers(1, 401)), d_model=64 * int(rng.integers(1, 9)),
+        n_routed=N, top_k=K, n_shared=n_shared, d_ff=64 * int(rng.integers(1, 5)),
+        d_ff_shared=64 * int(rng.integers(1, 4)), scoring=str(scoring),
+        renorm=bool(scoring in ("sigmoid", "sqrt_softplus") or rng.random() < 0.3),
+        dtype=dtype, bias=bool(scoring != "hash" and rng.random() < 0.5),
+        zipf_s=1.1 if (scoring != "hash" and rng.random() < 0.3) else 0.0, seed=i,
+        n_groups=groups, topk_groups=topk_groups)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_layer(i):
+    cfg = draw(i)
+    print(f"[random] {cfg}", flush=True)
+    inp = make_inputs(cfg, "cpu")
+    for k in ("x", "w_gate", "w13", "w2", "w13s", "w2s", "bias", "offset", "token_ids"):
+        v = getattr(inp, k)
+        if v is not None:
+            setattr(inp, k, v.cuda())
+    r = gpu_layer(cfg, inp)
+    idx, gate = check_routing_identical_logits(cfg, inp, r)
+    tokens = np.arange(cfg.T)
+    h_ref = oracle_h(cfg, inp, tokens, idx, gate)
+    if cfg.dtype == "bf16":
+        assert np.abs(h_ref).max() < 8.0, "outside the bar's range (bf16 half-ulp > 0.0156)"
+    res = compare_h(cfg, gpu_h_as_f64(r["h"]), h_ref, np.full(cfg.T, np.inf))
+    print(f"[random] {cfg.name}: max_abs {res[0]:.3g} rel_l2 {res[1]:.3g} excluded {res[2]}",
+          flush=True)

@@ -441,21 +441,76 @@ __global__ __launch_bounds__(P::NT) void k_gate_up_bf16(const GroupedArgs a) {
     }
 }
 
-// Byte offset of (row, col) in an fp16 output tile staged in LDS: rows of
-// BN halves; the 16-byte chunk c of row r sits at chunk c ^ (4 ((r >> 2) & 1)),
-// so the two row groups one staging write covers (lanes 0-31: rows r..,
-// lanes 32-63: rows r + 4..) fall in disjoint LDS banks.
+// Byte offset of the 16-byte chunk c (eight halves) of row `row` in an fp16
+// output tile staged in LDS: rows of BN halves (BN / 8 chunks); chunk c sits
+// in slot c ^ (row & 15).  The 16 lanes of one LDS pass that write one chunk
+// column of 16 consecutive rows, and the 16 that read 16 consecutive chunks
+// of one row, then hit 16 distinct 16-byte bank groups of the 64-bank LDS.
 template <class P>
-__device__ __forceinline__ int stage_offset(int row, int col) {
-    return 2 * (row * P::BN + ((((col >> 3) ^ (((row >> 2) & 1) << 2))) << 3) + (col & 7));
+__device__ __forceinline__ int stage_chunk(int row, int c) {
+    static_assert(P::BN / 8 >= 16 && (P::BN / 8) % 16 == 0, "chunk swizzle spans whole groups");
+    return row * (2 * P::BN) + ((c ^ (row & 15)) << 4);
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// fp16 of g * v for the 16 accumulator registers of one transposed fragment
+// (TR layout: this lane's row, four columns per register quad), packed two
+// halves per word, and then exchanged between lanes l and l + 32 (which hold
+// the two 4-column halves of each 8-column chunk of the same row): lane l
+// leaves with chunks 0 and 2 of the fragment's 32 columns, lane l + 32 with
+// chunks 1 and 3, each whole (pk[qp][0..1], pk[qp + 1][0..1] for the chunk
+// qp + (l >> 5), qp = 0, 2).  hm: running packed maximum of |half| bits of
+// this lane's values (0x7C00 and up: not finite).  Every lane of the wave
+// must take part (the exchange is a cross-lane move).
+__device__ __forceinline__ void pack_tr_fragment(const f32x16 &v, float g, bool valid,
+                                                 uint32_t (&pk)[4][2], u16x2 &hm) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const f16x2 h2 = {(_Float16)(g * v[4 * q + 2 * w]), (_Float16)(g * v[4 * q + 2 * w + 1])};
+            pk[q][w] = __builtin_bit_cast(uint32_t, h2);
+            const u16x2 m = __builtin_bit_cast(u16x2, valid ? (pk[q][w] & 0x7FFF7FFFu) : 0u);
+            hm = __builtin_elementwise_max(hm, m);
+        }
+    // permlane32_swap: the upper 32 lanes of the first operand trade places
+    // with the lower 32 lanes of the second
+#pragma unroll
+    for (int qp = 0; qp < 4; qp += 2)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(pk[qp][w], pk[qp + 1][w], false, false);
+            pk[qp][w] = sw[0];
+            pk[qp + 1][w] = sw[1];
+        }
+}
+
+// fp32 copies of the values of one transposed fragment that fp16 cannot hold
+// (rare; the combine reads them in place of the fp16 ones).
+template <class P>
+__device__ __forceinline__ void store_f32_marked(const f32x16 &v, float g, int tid, int j,
+                                                 int ncols, float *dst_row) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int col = pipe_out_col_tr<P>(tid, j, r);
+        const float w = g * v[r];
+        if (col < ncols && f16_marked(__builtin_bit_cast(uint16_t, (_Float16)w))) dst_row[col] = w;
+    }
 }
 
 // One down-projection tile whose wave computes NF row fragments.  Thread t
 // brings the destination row and gate of tile row t (fetched before the K
-// loop).  Epilogue: every wave writes fp16(gate * y) of its fragments into
-// the tile staged in LDS (the A stages and the first two B stages), then
-// each wave stores two whole rows of 512 bytes at a time with 16-byte lane
-// stores.  A value beyond fp16's range (rare) is also stored as fp32.
+// loop).  The MFMAs run transposed (TR), so a lane holds four consecutive
+// output columns of one row per register quad and one gate per fragment.
+// Epilogue: every wave packs fp16(gate * y) of its fragments, exchanges
+// halves across the wave (pack_tr_fragment) and writes whole 16-byte chunks
+// into the tile staged in LDS (the A stages and the first two B stages);
+// then each wave stores two whole rows of 512 bytes at a time with 16-byte
+// lane stores.  A value beyond fp16's range (rare) is also stored as fp32.
+// The next item is resolved before the stores are issued, so thread 0 waits
+// for the ticket's atomic alone, not for the stores' completion.
 //
 // FOLD: a split tile of at most 128 rows whose lo plane sits in the tile's
 // rows 128-255 (row 128 + r holds lo of row r; see down_body): each W2
@@ -473,26 +528,29 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     constexpr int FMASK = FOLD ? ((1 << NF) - 1) * 5 : (1 << NP) - 1;
     f32x16 acc[NP > 0 ? NP : 1][P::FN];
     if constexpr (F16) {
-        pipe_gemm_nf<P, false, NF, true, false, (1 << NF) - 1, true>(
+        pipe_gemm_nf<P, false, NF, true, false, (1 << NF) - 1, true, true>(
             lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, 0, acc);
     } else if constexpr (FOLD) {
         if (tj.shared)
-            pipe_gemm_nf<P, false, NP, false, STREAM_B, FMASK>(lds, rows, K, a.fs, a.n_shared,
-                                                               (size_t)a.d * a.fs, 0, acc);
+            pipe_gemm_nf<P, false, NP, false, STREAM_B, FMASK, false, true>(
+                lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, 0, acc);
         else
-            pipe_gemm_nf<P, false, NP, false, STREAM_B, FMASK>(lds, rows, K, 0, 1, 0, 0, acc);
+            pipe_gemm_nf<P, false, NP, false, STREAM_B, FMASK, false, true>(lds, rows, K, 0, 1, 0, 0,
+                                                                           acc);
 #pragma unroll
         for (int i = 0; i < NF; ++i)
 #pragma unroll
             for (int j = 0; j < P::FN; ++j) acc[i][j] += acc[i + 2][j];
     } else if (tj.shared) {
-        pipe_gemm_nf<P, false, NF, true, STREAM_B>(lds, rows, K, a.fs, a.n_shared,
-                                                   (size_t)a.d * a.fs, split ? K / 2 : 0, acc);
+        pipe_gemm_nf<P, false, NF, true, STREAM_B, (1 << NF) - 1, false, true>(
+            lds, rows, K, a.fs, a.n_shared, (size_t)a.d * a.fs, split ? K / 2 : 0, acc);
     } else {
-        pipe_gemm_nf<P, false, NF, true, STREAM_B>(lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
+        pipe_gemm_nf<P, false, NF, true, STREAM_B, (1 << NF) - 1, false, true>(
+            lds, rows, K, 0, 1, 0, split ? K / 2 : 0, acc);
     }
     int32_t *rdst = (int32_t *)(lds + tile_info_offset<P>());   // destination row
     float *rgate = (float *)(lds + tile_info_offset<P>() + 4 * P::BM);
+    int32_t *slot = (int32_t *)(lds + queue_slot_offset<P>());
     if (threadIdx.x < P::BM) {
         rdst[threadIdx.x] = tj.shared ? tj.row0 + (int)threadIdx.x : my_pair;
         rgate[threadIdx.x] = tj.shared ? 1.0f : my_gate;
@@ -502,94 +560,86 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     const int tid = opaque_tid();
     const int lane = tid & 63;
     const int ncols = min(P::BN, a.d - n0);
+    uint16_t *yh = tj.shared ? a.ysh : a.yrh;
+    float *yf = tj.shared ? a.ys : a.yr;
     if (tj.nrows <= 8) {
         // A tile of at most 8 rows (decode-sized groups): they all sit in
-        // accumulator registers 0-3 of fragment 0 of wave row 0 (rows 0-3 in
-        // lanes 0-31, rows 4-7 in lanes 32-63), stored directly, 2 bytes a
-        // lane, with no staging.
+        // fragment 0 of wave row 0 (rows 0-7 in lanes 0-7 and 32-39) and are
+        // stored straight from registers, 16 bytes a lane, with no staging.
+        if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
+        lds_barrier();
+        const int item = __builtin_amdgcn_readfirstlane(*slot);
         if (NF > 0 && P::wave_m(tid) == 0) {
-            uint16_t *yh = tj.shared ? a.ysh : a.yrh;
-            float *yf = tj.shared ? a.ys : a.yr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = (lane >> 5) * 4 + r;
-                if (row >= tj.nrows) continue;
-                const float g = rgate[row];
-                const size_t o = (size_t)rdst[row] * a.d + n0;
-#pragma unroll
-                for (int j = 0; j < P::FN; ++j) {
-                    const int col = pipe_out_col<P, false>(tid, j);
-                    const float w = g * acc[0][j][r];
-                    const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)w);
-                    if (col < ncols) {
-                        yh[o + col] = h;
-                        if (f16_marked(h)) yf[o + col] = w;
-                    }
-                }
-            }
-        }
-        return publish_item<P>(lds, a, k, ticket);
-    }
-    char *const st = lds;
-    uint32_t hmax = 0;   // largest |half| of a valid row: 0x7C00 and up = not finite
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-        const int rb = P::a_row(P::wave_m(tid), i) + (lane >> 5) * 4;   // + 8 q + s
-        float g[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 gq = *(const float4 *)(rgate + rb + 8 * q);
-            g[4 * q] = gq.x;
-            g[4 * q + 1] = gq.y;
-            g[4 * q + 2] = gq.z;
-            g[4 * q + 3] = gq.w;
-        }
-#pragma unroll
-        for (int j = 0; j < P::FN; ++j) {
-            const int col = pipe_out_col<P, false>(tid, j);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rb + 8 * (r >> 2) + (r & 3);
-                const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(g[r] * acc[i][j][r]));
-                hmax = max(hmax, row < tj.nrows ? (h & 0x7FFFu) : 0u);
-                *(uint16_t *)(st + stage_offset<P>(row, col)) = (uint16_t)h;
-            }
-        }
-    }
-    if (hmax >= 0x7C00u) {
-        // some value of this lane has no finite fp16 form: store it as fp32
-        float *yf = tj.shared ? a.ys : a.yr;
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            const int rb = P::a_row(P::wave_m(tid), i) + (lane >> 5) * 4;
+            const int row = pipe_out_row_tr<P>(tid, 0);   // lane & 31
+            const bool valid = row < tj.nrows;
+            const float g = rgate[row];
+            const size_t o = (size_t)rdst[valid ? row : 0] * a.d + n0;
+            u16x2 hm = {0, 0};
 #pragma unroll
             for (int j = 0; j < P::FN; ++j) {
-                const int col = pipe_out_col<P, false>(tid, j);
+                uint32_t pk[4][2];
+                pack_tr_fragment(acc[0][j], g, valid, pk, hm);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rb + 8 * (r >> 2) + (r & 3);
-                    const float w = rgate[row] * acc[i][j][r];
-                    if (row < tj.nrows && col < ncols &&
-                        f16_marked(__builtin_bit_cast(uint16_t, (_Float16)w)))
-                        yf[(size_t)rdst[row] * a.d + n0 + col] = w;
+                for (int qp = 0; qp < 4; qp += 2) {
+                    const int col = (P::wave_n(tid) * P::FN + j) * 32 + (qp + (lane >> 5)) * 8;
+                    if (valid && col < ncols)
+                        *(u32x4 *)(yh + o + col) = u32x4{pk[qp][0], pk[qp][1], pk[qp + 1][0], pk[qp + 1][1]};
                 }
+            }
+            if (valid && (hm[0] >= 0x7C00u || hm[1] >= 0x7C00u))
+#pragma unroll
+                for (int j = 0; j < P::FN; ++j) store_f32_marked<P>(acc[0][j], g, tid, j, ncols, yf + o);
+        }
+        return item;
+    }
+    char *const st = lds;
+    u16x2 hm = {0, 0};   // largest |half| of a valid row: 0x7C00 and up = not finite
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int row = pipe_out_row_tr<P>(tid, i);
+        const float g = rgate[row];
+        const bool valid = row < tj.nrows;
+#pragma unroll
+        for (int j = 0; j < P::FN; ++j) {
+            uint32_t pk[4][2];
+            pack_tr_fragment(acc[i][j], g, valid, pk, hm);
+#pragma unroll
+            for (int qp = 0; qp < 4; qp += 2) {
+                const int c = (P::wave_n(tid) * P::FN + j) * 4 + qp + (lane >> 5);
+                *(u32x4 *)(st + stage_chunk<P>(row, c)) =
+                    u32x4{pk[qp][0], pk[qp][1], pk[qp + 1][0], pk[qp + 1][1]};
             }
         }
     }
-    lds_barrier();   // the staged tile is complete
-    uint16_t *yh = tj.shared ? a.ysh : a.yrh;
+    if (hm[0] >= 0x7C00u || hm[1] >= 0x7C00u) {
+        // some value of this lane has no finite fp16 form: store it as fp32
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int row = pipe_out_row_tr<P>(tid, i);
+            if (row < tj.nrows) {
+                const float g = rgate[row];
+#pragma unroll
+                for (int j = 0; j < P::FN; ++j)
+                    store_f32_marked<P>(acc[i][j], g, tid, j, ncols, yf + (size_t)rdst[row] * a.d + n0);
+            }
+        }
+    }
+    if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
+    lds_barrier();   // the staged tile is complete and the next item published
     constexpr int CHUNKS = P::BN / 8;   // 16-byte chunks per row
 #pragma unroll 4
     for (int it = 0; it < P::BM * CHUNKS / P::NT; ++it) {
         const int q = it * P::NT + tid;
-        const int row = q / CHUNKS, c8 = (q % CHUNKS) * 8;
-        if (row < tj.nrows && c8 < ncols) {
+        const int row = q / CHUNKS, c = q % CHUNKS;
+        if (row < tj.nrows && c * 8 < ncols) {
             // read by the combine only, after this launch: not kept in cache
-            const u32x4 v = *(const u32x4 *)(st + stage_offset<P>(row, c8));
-            __builtin_nontemporal_store(v, (u32x4 *)(yh + (size_t)rdst[row] * a.d + n0 + c8));
+            const u32x4 v = *(const u32x4 *)(st + stage_chunk<P>(row, c));
+            __builtin_nontemporal_store(v, (u32x4 *)(yh + (size_t)rdst[row] * a.d + n0 + c * 8));
         }
     }
-    return publish_item<P>(lds, a, k, ticket);
+    const int item = __builtin_amdgcn_readfirstlane(*slot);
+    lds_barrier();   // every wave is done with the staged tile before the next prologue
+    return item;
 }
 
 template <class P>

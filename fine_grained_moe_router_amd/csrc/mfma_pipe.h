@@ -172,9 +172,13 @@ __device__ __forceinline__ void load_lds16_at(const uint16_t *base, uint32_t byt
 // read by this tile alone and once, so its loads are non-temporal.  FMASK:
 // which of the NF leading fragments the wave computes (all by default; a
 // folded split tile skips the fragments between its hi and lo rows).  F16:
-// both operands are fp16 (v_mfma_f32_32x32x16_f16) instead of bf16.
+// both operands are fp16 (v_mfma_f32_32x32x16_f16) instead of bf16.  TR:
+// the MFMAs take the B fragment as their first operand, so each accumulator
+// holds its block transposed: lane l owns tile row a_row(wm, i) + (l & 31)
+// and register r column b_row(wn, j) + 8 (r >> 2) + 4 (l >> 5) + (r & 3)
+// (four consecutive columns per register quad; see pipe_out_row_tr).
 template <class P, bool SPLIT, int NF, bool AFF = false, bool STREAM_B = false,
-          int FMASK = (1 << NF) - 1, bool F16 = false>
+          int FMASK = (1 << NF) - 1, bool F16 = false, bool TR = false>
 __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &rows, int K,
                                              int bsplit, int bmod, size_t bstride, int a_half,
                                              f32x16 (&acc)[NF > 0 ? NF : 1][P::FN]) {
@@ -335,9 +339,15 @@ __device__ __forceinline__ void pipe_gemm_nf(char *lds, const OperandRows<P> &ro
                     if (i == q && ((FMASK >> i) & 1))
 #pragma unroll
                         for (int j = 0; j < P::FN; ++j)
-                            if constexpr (F16)
+                            if constexpr (F16 && TR)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    b[cur][j], a[cur][i], acc[i][j], 0, 0, 0);
+                            else if constexpr (F16)
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                                     a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+                            else if constexpr (TR)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    b[cur][j], a[cur][i], acc[i][j], 0, 0, 0);
                             else
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                     a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
@@ -417,6 +427,16 @@ template <class P>
 __device__ __forceinline__ int pipe_out_row(int tid, int i, int r) {
     const int lane = tid & 63;
     return P::a_row(P::wave_m(tid), i) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+// Transposed accumulators (TR): tile row of fragment i (one per lane) and
+// tile column of register r of fragment j.
+template <class P>
+__device__ __forceinline__ int pipe_out_row_tr(int tid, int i) {
+    return P::a_row(P::wave_m(tid), i) + (tid & 31);
+}
+template <class P>
+__device__ __forceinline__ int pipe_out_col_tr(int tid, int j, int r) {
+    return (P::wave_n(tid) * P::FN + j) * 32 + (r >> 2) * 8 + ((tid & 63) >> 5) * 4 + (r & 3);
 }
 // SPLIT: hidden column (within a half) of gate/up pair j (< FN/2); else
 // column of the tile.

@@ -282,7 +282,7 @@ __device__ __forceinline__ void argmax_dpp_step(float &v, int &idx) {
         idx = oi;
     }
 }
-__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
+__device__ __forceinline__ void wave_argmax_pairs(float &v, int &idx) {
     argmax_dpp_step<0xB1, 0xF>(v, idx);    // quad_perm [1,0,3,2]: lane ^ 1
     argmax_dpp_step<0x4E, 0xF>(v, idx);    // quad_perm [2,3,0,1]: lane ^ 2
     argmax_dpp_step<0x141, 0xF>(v, idx);   // row_half_mirror: the two quads of 8 lanes
@@ -291,6 +291,35 @@ __device__ __forceinline__ void wave_argmax(float &v, int &idx) {
     argmax_dpp_step<0x143, 0xC>(v, idx);   // row_bcast:31 into rows 2, 3
     v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
     idx = __builtin_amdgcn_readlane(idx, 63);
+}
+
+// The same winner from a wave-wide maximum of v alone (one DPP max per step)
+// and a ballot of the lanes holding it: lanes own increasing expert ranges,
+// so among equal values the lowest such lane holds the lowest index.  Lanes
+// with no candidate (idx 0x7fffffff) are left out of the ballot; if no lane
+// matches (no candidate at all, or NaN values) the pairwise reduction above
+// decides.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float max_dpp_step(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                        __float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK, 0xF, false)));
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &idx) {
+    float m = v;
+    m = max_dpp_step<0xB1, 0xF>(m);
+    m = max_dpp_step<0x4E, 0xF>(m);
+    m = max_dpp_step<0x141, 0xF>(m);
+    m = max_dpp_step<0x140, 0xF>(m);
+    m = max_dpp_step<0x142, 0xA>(m);
+    m = max_dpp_step<0x143, 0xC>(m);
+    m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(v == m && idx != 0x7fffffff);
+    if (hit) {
+        idx = __builtin_amdgcn_readlane(idx, (int)__builtin_ctzll(hit));
+        v = m;
+    } else {
+        wave_argmax_pairs(v, idx);
+    }
 }
 
 // One wavefront per token.  Lane `lane` owns experts lane_expert(lane, j),
@@ -397,7 +426,8 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
                         mine = s32[j];
                     }
                 sel[k] = bi;
-                sv[k] = __shfl(mine, bi / J, kWave);   // the lane that owns expert bi
+                // from the lane that owns expert bi (bi is the same in every lane)
+                sv[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), (bi / J) & 63));
             }
         }
         // ---- gates: s, or s / (double sum of the selected s in k order)

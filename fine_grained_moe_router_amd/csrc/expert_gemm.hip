@@ -243,6 +243,30 @@ __device__ __forceinline__ void item_tile(const GroupedArgs &a, int item, int &m
     queue_item(a, q, item & ((1 << kItemBits) - 1), m, j, d);
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Transposed accumulators (TR) hold, in lanes l and l + 32, the two 4-column
+// halves of each 8-column chunk q of one row (pk[q][0..1]: two packed
+// 16-bit values each).  Exchange them so that lane l holds chunks 0 and 2
+// whole and lane l + 32 chunks 1 and 3: chunk qp + (l >> 5) is then
+// {pk[qp][0], pk[qp][1], pk[qp + 1][0], pk[qp + 1][1]} for qp = 0, 2.
+// permlane32_swap trades the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second.  Every lane of the wave must take part.
+__device__ __forceinline__ void swap_tr_halves(uint32_t (&pk)[4][2]) {
+#pragma unroll
+    for (int qp = 0; qp < 4; qp += 2)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(pk[qp][w], pk[qp + 1][w], false, false);
+            pk[qp][w] = sw[0];
+            pk[qp + 1][w] = sw[1];
+        }
+}
+__device__ __forceinline__ u32x4 tr_chunk(const uint32_t (&pk)[4][2], int qp) {
+    return u32x4{pk[qp][0], pk[qp][1], pk[qp + 1][0], pk[qp + 1][1]};
+}
+
 // 4x4 transpose across the four lanes of a quad (lanes 4q .. 4q+3): on
 // entry lane p holds column p of the block (v[r] = M[r][p]), on exit row p
 // (v[c] = M[p][c]).  Two exchange stages, lane ^ 1 then lane ^ 2, with DPP
@@ -452,9 +476,6 @@ __device__ __forceinline__ int stage_chunk(int row, int c) {
     return row * (2 * P::BN) + ((c ^ (row & 15)) << 4);
 }
 
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
 // fp16 of g * v for the 16 accumulator registers of one transposed fragment
 // (TR layout: this lane's row, four columns per register quad), packed two
 // halves per word, and then exchanged between lanes l and l + 32 (which hold
@@ -475,16 +496,7 @@ __device__ __forceinline__ void pack_tr_fragment(const f32x16 &v, float g, bool 
             const u16x2 m = __builtin_bit_cast(u16x2, valid ? (pk[q][w] & 0x7FFF7FFFu) : 0u);
             hm = __builtin_elementwise_max(hm, m);
         }
-    // permlane32_swap: the upper 32 lanes of the first operand trade places
-    // with the lower 32 lanes of the second
-#pragma unroll
-    for (int qp = 0; qp < 4; qp += 2)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(pk[qp][w], pk[qp + 1][w], false, false);
-            pk[qp][w] = sw[0];
-            pk[qp + 1][w] = sw[1];
-        }
+    swap_tr_halves(pk);
 }
 
 // fp32 copies of the values of one transposed fragment that fp16 cannot hold
@@ -583,7 +595,7 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
                 for (int qp = 0; qp < 4; qp += 2) {
                     const int col = (P::wave_n(tid) * P::FN + j) * 32 + (qp + (lane >> 5)) * 8;
                     if (valid && col < ncols)
-                        *(u32x4 *)(yh + o + col) = u32x4{pk[qp][0], pk[qp][1], pk[qp + 1][0], pk[qp + 1][1]};
+                        *(u32x4 *)(yh + o + col) = tr_chunk(pk, qp);
                 }
             }
             if (valid && (hm[0] >= 0x7C00u || hm[1] >= 0x7C00u))
@@ -606,8 +618,7 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
 #pragma unroll
             for (int qp = 0; qp < 4; qp += 2) {
                 const int c = (P::wave_n(tid) * P::FN + j) * 4 + qp + (lane >> 5);
-                *(u32x4 *)(st + stage_chunk<P>(row, c)) =
-                    u32x4{pk[qp][0], pk[qp][1], pk[qp + 1][0], pk[qp + 1][1]};
+                *(u32x4 *)(st + stage_chunk<P>(row, c)) = tr_chunk(pk, qp);
             }
         }
     }

@@ -29,20 +29,36 @@ namespace moe {
 template <int NF>
 __device__ __forceinline__ void router_tile(char *lds, const OperandRows<PipeTile> &rows, int K, int T,
                                             int N, int m0, int n0, float *__restrict__ out) {
-    f32x16 acc[NF > 0 ? NF : 1][PipeTile::FN];
-    pipe_gemm_nf<PipeTile, false, NF, true>(lds, rows, K, 0, 1, 0, 0, acc);
+    using P = PipeTile;
+    f32x16 acc[NF > 0 ? NF : 1][P::FN];
+    // transposed accumulators: a lane holds one token row and, per register
+    // quad, four consecutive experts, stored as one 16-byte write where the
+    // rows are 16-byte aligned (N' a multiple of 4, an aligned buffer)
+    pipe_gemm_nf<P, false, NF, true, false, (1 << NF) - 1, false, true>(lds, rows, K, 0, 1, 0, 0,
+                                                                       acc);
+    const bool wide = (N & 3) == 0 && ((uintptr_t)out & 15) == 0;
 #pragma unroll
-    for (int i = 0; i < NF; ++i)
+    for (int i = 0; i < NF; ++i) {
+        const int tid = opaque_tid();
+        const int row = m0 + pipe_out_row_tr<P>(tid, i);
+        if (row >= T) continue;
+        float *orow = out + (size_t)row * N;
 #pragma unroll
-        for (int j = 0; j < PipeTile::FN; ++j) {
-            const int tid = opaque_tid();
-            const int col = n0 + pipe_out_col<PipeTile, false>(tid, j);
+        for (int j = 0; j < P::FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + pipe_out_row<PipeTile>(tid, i, r);
-                if (row < T && col < N) out[(size_t)row * N + col] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + pipe_out_col_tr<P>(tid, j, 4 * q);
+                if (wide) {
+                    if (col < N)
+                        *(f32x4 *)(orow + col) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                       acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        if (col + s < N) orow[col + s] = acc[i][j][4 * q + s];
+                }
             }
-        }
+    }
 }
 
 __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int N, int kps,

@@ -61,18 +61,20 @@ __device__ __forceinline__ void router_tile(char *lds, const OperandRows<PipeTil
     }
 }
 
-__global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int N, int kps,
+__global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int N, int kps, int rb,
                                                               size_t stride,
                                                               const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ wg,
                                                               float *__restrict__ out) {
     __shared__ __attribute__((aligned(16))) char lds[PipeTile::LDS_BYTES];
     using P = PipeTile;
-    const int m0 = blockIdx.x * P::BM, n0 = blockIdx.y * P::BN;
+    // rb (256 or 128) token rows per block: a half tile computes half the
+    // fragments (wave_frags), so twice the row blocks need half the K splits
+    const int m0 = blockIdx.x * rb, n0 = blockIdx.y * P::BN;
     const int k0 = blockIdx.z * kps * P::BK;
     const int K = min(d - k0, kps * P::BK);
     out += (size_t)blockIdx.z * stride;
-    const int nrows = min(P::BM, T - m0);
+    const int nrows = min(rb, T - m0);
     // Both operands are affine: token rows m0.. and expert rows n0.. (token
     // rows past T are not fetched; expert rows past N' fetch row N' - 1).
     OperandRows<P> rows;
@@ -114,12 +116,22 @@ __global__ __launch_bounds__(256) void k_router_f32(int T, int d, int N, const f
         }
 }
 
-// K splits of the bf16 router GEMM: enough blocks to cover the CUs (one
-// 256 x 256 tile per CU), each split at least 8 k-tiles long.
-int router_splits(const moe_config &c) {
-    if (c.dtype != MOE_BF16) return 1;
+// Token rows per block of the bf16 router GEMM: 128 where 256-row tiles
+// would need more than four K splits to cover the CUs (half the splits,
+// half the partial sums written and read back by the selection), else 256.
+int router_rows_per_block(const moe_config &c) {
     const int tiles = ((c.T + PipeTile::BM - 1) / PipeTile::BM) *
                       ((c.n_routed + PipeTile::BN - 1) / PipeTile::BN);
+    return (c.T > PipeTile::BM / 2 && (device_cu_count() + tiles - 1) / tiles > 4) ? PipeTile::BM / 2
+                                                                                   : PipeTile::BM;
+}
+
+// K splits of the bf16 router GEMM: enough blocks to cover the CUs (one
+// tile per CU), each split at least 8 k-tiles long.
+int router_splits(const moe_config &c) {
+    if (c.dtype != MOE_BF16) return 1;
+    const int rb = router_rows_per_block(c);
+    const int tiles = ((c.T + rb - 1) / rb) * ((c.n_routed + PipeTile::BN - 1) / PipeTile::BN);
     const int nk = c.d_model / PipeTile::BK;
     int z = min(min(16, nk / 8), (device_cu_count() + tiles - 1) / tiles);
     if (z <= 1) return 1;
@@ -133,10 +145,11 @@ hipError_t launch_router_logits(const moe_config &c, const void *x, const void *
     if (c.dtype == MOE_BF16) {
         const int nk = c.d_model / PipeTile::BK;
         const int kps = (nk + z - 1) / z;
-        dim3 grid((c.T + PipeTile::BM - 1) / PipeTile::BM,
-                  (c.n_routed + PipeTile::BN - 1) / PipeTile::BN, z);
+        const int rb = router_rows_per_block(c);
+        dim3 grid((c.T + rb - 1) / rb, (c.n_routed + PipeTile::BN - 1) / PipeTile::BN, z);
         hipLaunchKernelGGL(k_router_bf16, grid, dim3(PipeTile::NT), 0, s, c.T, c.d_model,
-                           c.n_routed, kps, stride, (const uint16_t *)x, (const uint16_t *)wg, out);
+                           c.n_routed, kps, rb, stride, (const uint16_t *)x, (const uint16_t *)wg,
+                           out);
     } else {
         dim3 grid((c.T + 63) / 64, (c.n_routed + 63) / 64);
         hipLaunchKernelGGL(k_router_f32, grid, dim3(256), 0, s, c.T, c.d_model, c.n_routed,

@@ -306,8 +306,8 @@ def pmc_summary(out_dir: str, workload: str, stage: str = "gate_up"):
            "counters": res, "traffic_bytes_per_launch": traffic,
            "copy_bytes": COPY_BYTES, "source_digest": source_digest(),
            "commands": [
-               f"rocprofv3 --pmc FETCH_SIZE -d {out_dir}/fetch -- python3 bench.py --pmc-run --workload {workload}",
-               f"rocprofv3 --pmc WRITE_SIZE -d {out_dir}/write -- python3 bench.py --pmc-run --workload {workload}",
+               f"rocprofv3 --pmc FETCH_SIZE -d {out_dir}/fetch -o run --output-format csv -- python3 bench.py --pmc-run --workload {workload}",
+               f"rocprofv3 --pmc WRITE_SIZE -d {out_dir}/write -o run --output-format csv -- python3 bench.py --pmc-run --workload {workload}",
                f"python3 bench.py --pmc-summary {out_dir} --workload {workload}"]}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(traffic_record_path(workload, stage), "w") as fh:

@@ -1,7 +1,8 @@
 """Seeded random layer configurations against the oracle, end to end.
 
 Each case draws a small layer from the API's whole space: bf16 or fp32;
-1..400 tokens; d and d_ff from 64 to 512 / 256 (multiples of 64); 1..256
+1..400 tokens (1..1200 from case 24 on: several router row blocks
+and GEMM row tiles per expert); d and d_ff from 64 to 512 / 256 (multiples of 64); 1..256
 routed experts with K' up to 16; 0..2 shared experts; softmax, sigmoid,
 sqrt(softplus) or hash scoring, with or without renormalisation, selection
 bias and a Zipf logit offset; and, for a third of the learned routings, a
@@ -22,7 +23,7 @@ from parity import check_routing_identical_logits, compare_h, gpu_h_as_f64, gpu_
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 40
 
 
 def draw(i):
@@ -40,7 +41,7 @@ def draw(i):
             need = -(-K // (N // groups))          # groups needed to hold K' experts
             topk_groups = int(rng.integers(need, groups + 1))
     return LayerConfig(
-        name=f"rand{i:02d}", T=int(rng.integers(1, 401)), d_model=64 * int(rng.integers(1, 9)),
+        name=f"rand{i:02d}", T=int(rng.integers(1, 401 if i < 24 else 1201)), d_model=64 * int(rng.integers(1, 9)),
         n_routed=N, top_k=K, n_shared=n_shared, d_ff=64 * int(rng.integers(1, 5)),
         d_ff_shared=64 * int(rng.integers(1, 4)), scoring=str(scoring),
         renorm=bool(scoring in ("sigmoid", "sqrt_softplus") or rng.random() < 0.3),

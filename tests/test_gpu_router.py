@@ -19,17 +19,17 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # one 256-expert column tile, d split 8 ways on 256 CUs
+    # one 256-expert column tile, 128-token row blocks, d split 4 ways on 256 CUs
     "v3_prefill": CONFIGS["v3_prefill"],
-    # one partial row tile (64 tokens), d split to fill the device
+    # one partial 256-row tile (64 tokens), d split to fill the device
     "v3_decode": CONFIGS["v3_decode"],
-    # 384 experts: a second, half-empty column tile
+    # 384 experts: a second, half-empty column tile; 256-token row tiles
     "v4_skew": CONFIGS["v4_skew"],
-    # 64 experts (softmax, one per lane): a mostly empty column tile
+    # 64 experts (softmax, one per lane): a mostly empty column tile; 128-token row blocks
     "mid": CONFIGS["mid"],
     # 385 experts: a second column tile with 129 valid rows
     "n385": scaled(CONFIGS["v3_prefill"], T=4096, d_model=512, d_ff=128).with_(n_routed=385),
-    # a ragged row tile (333 = 256 + 77 tokens), two d ranges
+    # ragged row blocks (333 = 128 + 128 + 77 tokens), two d ranges
     "ragged": scaled(CONFIGS["v3_prefill"], T=333, d_model=1024, d_ff=128),
     # d of 4 k-tiles: no split
     "narrow": scaled(CONFIGS["mid"], T=700, d_model=256, d_ff=64),

@@ -637,18 +637,33 @@ __device__ __forceinline__ int down_tile(const GroupedArgs &a, const TileJob &tj
     }
     if (threadIdx.x == 0) *slot = resolve_ticket(a, k, ticket);
     lds_barrier();   // the staged tile is complete and the next item published
+    const int item = __builtin_amdgcn_readfirstlane(*slot);
     constexpr int CHUNKS = P::BN / 8;   // 16-byte chunks per row
-#pragma unroll 4
-    for (int it = 0; it < P::BM * CHUNKS / P::NT; ++it) {
-        const int q = it * P::NT + tid;
-        const int row = q / CHUNKS, c = q % CHUNKS;
-        if (row < tj.nrows && c * 8 < ncols) {
+    constexpr int ITERS = P::BM * CHUNKS / P::NT, BATCH = 4;
+    static_assert(ITERS % BATCH == 0, "whole batches");
+    // BATCH rows' chunks and destinations are read from LDS before any is
+    // stored (rows past the tile's end read stale values and are not
+    // stored), so the LDS latency is paid once per batch, not once per row
+#pragma unroll
+    for (int it0 = 0; it0 < ITERS; it0 += BATCH) {
+        u32x4 v[BATCH];
+        int dr[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int q = (it0 + u) * P::NT + tid;
+            const int row = q / CHUNKS, c = q % CHUNKS;
+            v[u] = *(const u32x4 *)(st + stage_chunk<P>(row, c));
+            dr[u] = rdst[row];
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int q = (it0 + u) * P::NT + tid;
+            const int row = q / CHUNKS, c = q % CHUNKS;
             // read by the combine only, after this launch: not kept in cache
-            const u32x4 v = *(const u32x4 *)(st + stage_chunk<P>(row, c));
-            __builtin_nontemporal_store(v, (u32x4 *)(yh + (size_t)rdst[row] * a.d + n0 + c * 8));
+            if (row < tj.nrows && c * 8 < ncols)
+                __builtin_nontemporal_store(v[u], (u32x4 *)(yh + (size_t)dr[u] * a.d + n0 + c * 8));
         }
     }
-    const int item = __builtin_amdgcn_readfirstlane(*slot);
     lds_barrier();   // every wave is done with the staged tile before the next prologue
     return item;
 }

@@ -428,13 +428,15 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
                 if (e < N && !((chosen >> (e / gsz)) & 1ull)) taken |= 1u << j;
             }
         }
-        // ---- top-K': K' rounds of a wave-wide argmax on (key desc, index asc)
-        int sel[kMaxTopK];
-        float sv[kMaxTopK];
+        // ---- top-K': K' rounds of a wave-wide argmax on (key desc, index asc).
+        // Lane k keeps round k's winner and its score (two registers, not
+        // K'-long arrays in every lane); the renormalisation's double sum
+        // of the selected s runs in round order as the rounds go.
+        int my_sel = 0;
+        float my_sv = 0.0f;
+        double den = 0.0;
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) {
-            sel[k] = 0;
-            sv[k] = 0.0f;
             if (k < K) {
                 float bk = -INFINITY;
                 int bi = 0x7fffffff;
@@ -454,24 +456,22 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select(
                         taken |= 1u << j;
                         mine = s32[j];
                     }
-                sel[k] = bi;
                 // from the lane that owns expert bi (bi is the same in every lane)
-                sv[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), (bi / J) & 63));
+                const float svk =
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), (bi / J) & 63));
+                den += (double)svk;
+                if (lane == k) {
+                    my_sel = bi;
+                    my_sv = svk;
+                }
             }
         }
         // ---- gates: s, or s / (double sum of the selected s in k order)
-        double den = 0.0;
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k)
-            if (k < K) den += (double)sv[k];
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            if (k < K && lane == k) {
-                const float g = renorm ? (float)((double)sv[k] / den) : sv[k];
-                idx_out[(size_t)t * K + k] = sel[k];
-                w_out[(size_t)t * K + k] = g;
-                atomicAdd(&hist[sel[k]], 1);
-            }
+        if (lane < K) {
+            const float g = renorm ? (float)((double)my_sv / den) : my_sv;
+            idx_out[(size_t)t * K + lane] = my_sel;
+            w_out[(size_t)t * K + lane] = g;
+            atomicAdd(&hist[my_sel], 1);
         }
     }
     // ---- this block's expert histogram and partial sums of s (waves added

@@ -322,30 +322,37 @@ __device__ __forceinline__ void wave_argmax_pairs(float &v, int &idx) {
     idx = __builtin_amdgcn_readlane(idx, 63);
 }
 
-// The same winner from a wave-wide maximum of v alone (one DPP max per step)
-// and a ballot of the lanes holding it: lanes own increasing expert ranges,
-// so among equal values the lowest such lane holds the lowest index.  Lanes
-// with no candidate (idx 0x7fffffff) are left out of the ballot; if no lane
-// matches (no candidate at all, or NaN values) the pairwise reduction above
-// decides.
+// The same winner from a wave-wide maximum of the key alone and a ballot
+// of the lanes holding it: lanes own increasing expert ranges, so among
+// equal keys the lowest such lane holds the lowest index.  The maximum runs
+// on 32-bit integers that order like the floats (sign-magnitude folded to
+// two's complement, -0 taken as +0 so that equal keys stay equal), one DPP
+// max per step.  Lanes with no candidate (idx 0x7fffffff) and NaN keys take
+// INT_MIN and never win; if no lane has a candidate left the pairwise
+// reduction above decides.
+__device__ __forceinline__ int ordered_key(float f) {
+    f = f + 0.0f;   // -0 -> +0
+    const int b = __float_as_int(f);
+    return (f != f) ? INT_MIN : (b ^ ((b >> 31) & 0x7FFFFFFF));
+}
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float max_dpp_step(float v) {
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
-                        __float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK, 0xF, false)));
+__device__ __forceinline__ int max_dpp_step(int v) {
+    return max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, CTRL, ROW_MASK, 0xF, false));
 }
 __device__ __forceinline__ void wave_argmax(float &v, int &idx) {
-    float m = v;
+    const int o = idx != 0x7fffffff ? ordered_key(v) : INT_MIN;
+    int m = o;
     m = max_dpp_step<0xB1, 0xF>(m);
     m = max_dpp_step<0x4E, 0xF>(m);
     m = max_dpp_step<0x141, 0xF>(m);
     m = max_dpp_step<0x140, 0xF>(m);
     m = max_dpp_step<0x142, 0xA>(m);
     m = max_dpp_step<0x143, 0xC>(m);
-    m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(v == m && idx != 0x7fffffff);
-    if (hit) {
-        idx = __builtin_amdgcn_readlane(idx, (int)__builtin_ctzll(hit));
-        v = m;
+    m = __builtin_amdgcn_readlane(m, 63);
+    if (m != INT_MIN) {
+        const int w = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(o == m));
+        idx = __builtin_amdgcn_readlane(idx, w);
+        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), w));
     } else {
         wave_argmax_pairs(v, idx);
     }

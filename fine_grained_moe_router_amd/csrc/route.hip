@@ -88,7 +88,11 @@ __global__ __launch_bounds__(PipeTile::NT) void k_router_bf16(int T, int d, int 
     rows.azero = pad_row_mask<P>(nrows);
     rows.bmask = valid_row_mask<P>(N - n0);
     rows.blast = (uint32_t)(N - 1) * (uint32_t)d;
-    switch (wave_frags<P>(nrows)) {
+    // a wave whose experts (its FN fragments of 32 columns) all lie past N'
+    // -- the rest of a ragged last column tile, or all but the first wave
+    // column for N' <= 64 -- issues no MFMAs (its loads and barriers stay)
+    const bool cols = n0 + P::wave_n(threadIdx.x) * P::FN * 32 < N;
+    switch (cols ? wave_frags<P>(nrows) : 0) {
         case 4: return router_tile<4>(lds, rows, K, T, N, m0, n0, out);
         case 3: return router_tile<3>(lds, rows, K, T, N, m0, n0, out);
         case 2: return router_tile<2>(lds, rows, K, T, N, m0, n0, out);
